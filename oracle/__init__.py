@@ -68,6 +68,7 @@ def lib():
             _P(ctypes.c_double), _P(ctypes.c_int64)
         i32, i64 = ctypes.c_int, ctypes.c_int64
         sig = {
+            "orc_num_threads": (ctypes.c_int, []),
             "orc_e4m3": (ctypes.c_double, [ctypes.c_uint8]),
             "orc_e2m1": (ctypes.c_double, [ctypes.c_uint8]),
             "orc_bf16": (ctypes.c_double, [ctypes.c_uint16]),
@@ -103,6 +104,11 @@ def _ptr(a: np.ndarray, ctype):
 
 
 # ---------------------------------------------------------------- scalars
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().orc_num_threads())
+
 
 def e4m3_value(code: int) -> float:
     return lib().orc_e4m3(int(code) & 0xFF)

@@ -38,10 +38,14 @@
  * single correctly rounded binary32 operations.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <string.h>
 
 #define ORC_API __attribute__((visibility("default")))
+
+/* Threads the OpenMP loops below use (reported next to oracle timings). */
+ORC_API int orc_num_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------ */
 /* Exact decoders                                                      */

@@ -1,0 +1,264 @@
+"""Python binding of libqhead.so: few-row quantized-weight LM-head GEMV on MI355X.
+
+Thin ctypes marshalling over the C ABI declared in ``include/qhead.h``: every
+function takes torch tensors that live in device memory, passes their data
+pointers and torch's current HIP stream, and raises ``QheadError`` on a
+negative status. All arithmetic runs in the HIP kernels of the library; there
+is no CPU path. Importing this module fails loudly when the library has not
+been built (``python quantized_weight_decode_amd/build.py`` or
+``__graft_entry__.build()``).
+
+Tensors: BF16 activations and logits may be ``torch.bfloat16`` or 16-bit
+integer tensors holding BF16 bits; E4M3 / packed FP4 / Q6_K / q8_1 bytes are
+``torch.uint8``; scales are ``torch.float32``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqhead.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "qhead.h")
+
+FMT_FP8, FMT_W8A8, FMT_NVFP4, FMT_Q6K = 0, 1, 2, 3
+Q8_BLOCK_BYTES = 36
+Q6K_BLOCK_BYTES = 210
+
+_STATUS_NAMES = {0: "QHEAD_OK", -1: "QHEAD_ERR_NULL", -2: "QHEAD_ERR_SHAPE",
+                 -3: "QHEAD_ERR_ALIGN", -4: "QHEAD_ERR_WORKSPACE", -5: "QHEAD_ERR_ARG",
+                 -6: "QHEAD_ERR_DEVICE", -7: "QHEAD_ERR_HIP"}
+
+
+class QheadError(RuntimeError):
+    def __init__(self, status: int, func: str):
+        self.status = status
+        super().__init__(f"{func}: {_STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libqhead.so not found at {LIB_PATH}; build it first with "
+        "`python quantized_weight_decode_amd/build.py` (hipcc, gfx950)")
+
+_vp, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+_SIGS = {
+    "qhead_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "qhead_max_rows_per_launch": (ctypes.c_int, [_i32]),
+    "qhead_plan_chunks": (ctypes.c_int, [_i32, _i32, ctypes.POINTER(_i32), _i32]),
+    "qhead_fp8_rowscale": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "qhead_quant_act_e4m3": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
+    "qhead_w8a8_workspace_bytes": (_sz, [_i32]),
+    "qhead_w8a8_gemv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "qhead_w8a8": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "qhead_nvfp4": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _f32, _vp]),
+    "qhead_quant_q8_1": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
+    "qhead_q6k_workspace_bytes": (_sz, [_i32]),
+    "qhead_q6k_gemv": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "qhead_q6k": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "qhead_quantize_fp8_rows": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
+}
+
+_lib = ctypes.CDLL(LIB_PATH)
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library, with argtypes set (raw pointer calls)."""
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/qhead.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qhead_[a-z0-9_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return _lib.qhead_status_string(int(status)).decode()
+
+
+def _check(status: int, func: str) -> None:
+    if status != 0:
+        raise QheadError(status, func)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtypes) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be in device memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t.data_ptr()
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_U8 = (torch.uint8,)
+_F32 = (torch.float32,)
+
+
+def max_rows_per_launch(fmt: int) -> int:
+    r = _lib.qhead_max_rows_per_launch(fmt)
+    _check(min(r, 0), "qhead_max_rows_per_launch")
+    return r
+
+
+def plan_chunks(fmt: int, rows: int) -> list[int]:
+    n = _lib.qhead_plan_chunks(fmt, rows, None, 0)
+    _check(min(n, 0), "qhead_plan_chunks")
+    buf = (_i32 * max(n, 1))()
+    n2 = _lib.qhead_plan_chunks(fmt, rows, buf, n)
+    _check(min(n2, 0), "qhead_plan_chunks")
+    return [buf[i] for i in range(n2)]
+
+
+def _out(out, rows, vocab, device):
+    if out is None:
+        out = torch.empty((rows, vocab), dtype=torch.bfloat16, device=device)
+    return out
+
+
+def fp8_rowscale(w: torch.Tensor, row_scale: torch.Tensor, x: torch.Tensor, out=None,
+                 stream=None) -> torch.Tensor:
+    """logits[rows, vocab] (BF16) from FP8 E4M3 weights [vocab, hidden] with F32 row scales."""
+    vocab, hidden = w.shape
+    rows = x.shape[0]
+    out = _out(out, rows, vocab, w.device)
+    st = _lib.qhead_fp8_rowscale(_dev(w, "w", _U8), _dev(row_scale, "row_scale", _F32),
+                                 _dev(x, "x", _BF16), rows, hidden, vocab,
+                                 _dev(out, "out", _BF16), _stream(stream))
+    _check(st, "qhead_fp8_rowscale")
+    return out
+
+
+def quant_act_e4m3(x: torch.Tensor, xq=None, xscale=None, stream=None):
+    """Per-row E4M3 activations: returns (xq uint8 [rows, hidden], xscale f32 [rows])."""
+    rows, hidden = x.shape
+    if xq is None:
+        xq = torch.empty((rows, hidden), dtype=torch.uint8, device=x.device)
+    if xscale is None:
+        xscale = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    st = _lib.qhead_quant_act_e4m3(_dev(x, "x", _BF16), rows, hidden, _dev(xq, "xq", _U8),
+                                   _dev(xscale, "xscale", _F32), _stream(stream))
+    _check(st, "qhead_quant_act_e4m3")
+    return xq, xscale
+
+
+def w8a8_workspace_bytes(hidden: int) -> int:
+    return int(_lib.qhead_w8a8_workspace_bytes(hidden))
+
+
+def w8a8_workspace(hidden: int, device) -> torch.Tensor:
+    return torch.empty((w8a8_workspace_bytes(hidden),), dtype=torch.uint8, device=device)
+
+
+def w8a8_gemv(w, row_scale, xq, xscale, out=None, stream=None) -> torch.Tensor:
+    vocab, hidden = w.shape
+    rows = xq.shape[0]
+    out = _out(out, rows, vocab, w.device)
+    st = _lib.qhead_w8a8_gemv(_dev(w, "w", _U8), _dev(row_scale, "row_scale", _F32),
+                              _dev(xq, "xq", _U8), _dev(xscale, "xscale", _F32), rows, hidden,
+                              vocab, _dev(out, "out", _BF16), _stream(stream))
+    _check(st, "qhead_w8a8_gemv")
+    return out
+
+
+def w8a8(w, row_scale, x, out=None, workspace=None, stream=None) -> torch.Tensor:
+    """W8A8 logits: per-row E4M3 activations, then FP8 x FP8 over the same weight bytes."""
+    vocab, hidden = w.shape
+    rows = x.shape[0]
+    out = _out(out, rows, vocab, w.device)
+    if workspace is None:
+        workspace = w8a8_workspace(hidden, w.device)
+    st = _lib.qhead_w8a8(_dev(w, "w", _U8), _dev(row_scale, "row_scale", _F32),
+                         _dev(x, "x", _BF16), rows, hidden, vocab, _dev(out, "out", _BF16),
+                         _dev(workspace, "workspace", _U8), workspace.numel(), _stream(stream))
+    _check(st, "qhead_w8a8")
+    return out
+
+
+def nvfp4(w_packed, block_scale, x, global_scale: float, out=None, stream=None) -> torch.Tensor:
+    """NVFP4 W4A16 logits; w_packed [vocab, hidden/2], block_scale [vocab, hidden/16]."""
+    vocab = w_packed.shape[0]
+    hidden = w_packed.shape[1] * 2
+    rows = x.shape[0]
+    out = _out(out, rows, vocab, w_packed.device)
+    st = _lib.qhead_nvfp4(_dev(w_packed, "w_packed", _U8), _dev(block_scale, "block_scale", _U8),
+                          _dev(x, "x", _BF16), rows, hidden, vocab, _dev(out, "out", _BF16),
+                          float(global_scale), _stream(stream))
+    _check(st, "qhead_nvfp4")
+    return out
+
+
+def quant_q8_1(x, q8=None, stream=None) -> torch.Tensor:
+    """block_q8_1 activations: uint8 [rows, hidden/32*36]."""
+    rows, hidden = x.shape
+    if q8 is None:
+        q8 = torch.empty((rows, hidden // 32 * Q8_BLOCK_BYTES), dtype=torch.uint8, device=x.device)
+    st = _lib.qhead_quant_q8_1(_dev(x, "x", _BF16), rows, hidden, _dev(q8, "q8", _U8),
+                               _stream(stream))
+    _check(st, "qhead_quant_q8_1")
+    return q8
+
+
+def q6k_workspace_bytes(hidden: int) -> int:
+    return int(_lib.qhead_q6k_workspace_bytes(hidden))
+
+
+def q6k_gemv(blocks, q8, hidden: int, out=None, stream=None) -> torch.Tensor:
+    vocab = blocks.shape[0]
+    rows = q8.shape[0]
+    out = _out(out, rows, vocab, blocks.device)
+    st = _lib.qhead_q6k_gemv(_dev(blocks, "blocks", _U8), _dev(q8, "q8", _U8), rows, hidden, vocab,
+                             _dev(out, "out", _BF16), _stream(stream))
+    _check(st, "qhead_q6k_gemv")
+    return out
+
+
+def q6k(blocks, x, out=None, workspace=None, stream=None) -> torch.Tensor:
+    """Q6_K logits: x quantized to q8_1 per <= 8-row chunk, then the Q6_K GEMV."""
+    vocab = blocks.shape[0]
+    rows, hidden = x.shape
+    out = _out(out, rows, vocab, blocks.device)
+    if workspace is None:
+        workspace = torch.empty((q6k_workspace_bytes(hidden),), dtype=torch.uint8,
+                                device=blocks.device)
+    st = _lib.qhead_q6k(_dev(blocks, "blocks", _U8), None, _dev(x, "x", _BF16), rows, hidden,
+                        vocab, _dev(out, "out", _BF16), _dev(workspace, "workspace", _U8),
+                        workspace.numel(), _stream(stream))
+    _check(st, "qhead_q6k")
+    return out
+
+
+def quantize_fp8_rows(w_f32: torch.Tensor, codes=None, scales=None, stream=None):
+    """Load-time per-row E4M3 quantization of F32 weights: (codes uint8, row scales f32)."""
+    vocab, hidden = w_f32.shape
+    if codes is None:
+        codes = torch.empty((vocab, hidden), dtype=torch.uint8, device=w_f32.device)
+    if scales is None:
+        scales = torch.empty((vocab,), dtype=torch.float32, device=w_f32.device)
+    st = _lib.qhead_quantize_fp8_rows(_dev(w_f32, "w_f32", _F32), vocab, hidden,
+                                      _dev(codes, "codes", _U8), _dev(scales, "scales", _F32),
+                                      _stream(stream))
+    _check(st, "qhead_quantize_fp8_rows")
+    return codes, scales

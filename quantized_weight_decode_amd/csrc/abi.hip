@@ -1,0 +1,319 @@
+// abi.hip -- the extern "C" entry points of libqhead.so (declared in
+// include/qhead.h): argument validation, the row-chunk planner, the device
+// check and the per-format chunk loops.
+//
+// Validation happens before any HIP call, so a rejected call touches no
+// device state. The chunk loops advance x by done*hidden and out by
+// done*vocab elements per chunk, as the chunk loops of lm_head_fp8_run
+// ("lm_head_fp8_rows.rs") and lm_head_q6k_run ("lm_head_q6k.rs") do.
+#include <mutex>
+#include <string.h>
+
+#include "../../include/qhead.h"
+#include "qhead_internal.h"
+
+namespace qh {
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mutex;
+DeviceInfo g_dev[kMaxDevices];
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int max_rows(int32_t format) {
+    switch (format) {
+        case QHEAD_FMT_FP8:
+            return 16;
+        case QHEAD_FMT_W8A8:
+            return 128;
+        case QHEAD_FMT_NVFP4:
+            return 8;
+        case QHEAD_FMT_Q6K:
+            return 8;
+        default:
+            return -1;
+    }
+}
+
+// Rows per launch of the W8A8 GEMV kernel inside one 128-row chunk.
+constexpr int kW8A8GemvRows = 16;
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? QHEAD_OK : QHEAD_ERR_HIP; }
+
+int device_or_error(DeviceInfo* dev) {
+    if (current_device(dev) != hipSuccess) return QHEAD_ERR_HIP;
+    if (!dev->is_gfx950 || dev->num_cus <= 0) return QHEAD_ERR_DEVICE;
+    return QHEAD_OK;
+}
+
+}  // namespace
+
+hipError_t current_device(DeviceInfo* out) {
+    int id = 0;
+    hipError_t e = hipGetDevice(&id);
+    if (e != hipSuccess) return e;
+    if (id < 0 || id >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (g_dev[id].device != id) {
+        DeviceInfo info;
+        info.device = id;
+        e = hipDeviceGetAttribute(&info.num_cus, hipDeviceAttributeMultiprocessorCount, id);
+        if (e != hipSuccess) return e;
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, id);
+        if (e != hipSuccess) return e;
+        info.is_gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        g_dev[id] = info;
+    }
+    *out = g_dev[id];
+    return hipSuccess;
+}
+
+}  // namespace qh
+
+using namespace qh;
+
+extern "C" {
+
+const char* qhead_status_string(int status) {
+    switch (status) {
+        case QHEAD_OK:
+            return "ok";
+        case QHEAD_ERR_NULL:
+            return "null pointer argument";
+        case QHEAD_ERR_SHAPE:
+            return "invalid shape (rows < 0, hidden/vocab <= 0, or hidden not a multiple of the "
+                   "format's granule)";
+        case QHEAD_ERR_ALIGN:
+            return "pointer not aligned as required";
+        case QHEAD_ERR_WORKSPACE:
+            return "workspace missing or too small";
+        case QHEAD_ERR_ARG:
+            return "invalid argument";
+        case QHEAD_ERR_DEVICE:
+            return "current device is not gfx950 (MI355X)";
+        case QHEAD_ERR_HIP:
+            return "HIP call or kernel launch failed";
+        default:
+            return "unknown status";
+    }
+}
+
+int qhead_max_rows_per_launch(int32_t format) {
+    int m = max_rows(format);
+    return m > 0 ? m : QHEAD_ERR_ARG;
+}
+
+int qhead_plan_chunks(int32_t format, int32_t rows, int32_t* chunk_rows, int32_t max_chunks) {
+    const int m = max_rows(format);
+    if (m <= 0) return QHEAD_ERR_ARG;
+    if (rows < 0) return QHEAD_ERR_SHAPE;
+    if (max_chunks < 0 || (max_chunks > 0 && chunk_rows == nullptr)) return QHEAD_ERR_NULL;
+    int n = 0;
+    for (int32_t done = 0; done < rows; ++n) {
+        const int32_t c = (rows - done) < m ? (rows - done) : m;
+        if (n < max_chunks) chunk_rows[n] = c;
+        done += c;
+    }
+    return n;
+}
+
+int qhead_fp8_rowscale(const uint8_t* w_e4m3, const float* row_scale, const uint16_t* x_bf16,
+                       int32_t rows, int32_t hidden, int32_t vocab, uint16_t* out_bf16,
+                       void* stream) {
+    if (rows < 0 || hidden <= 0 || vocab <= 0 || hidden % 16) return QHEAD_ERR_SHAPE;
+    if (rows == 0) return QHEAD_OK;
+    if (!w_e4m3 || !row_scale || !x_bf16 || !out_bf16) return QHEAD_ERR_NULL;
+    if (!aligned(w_e4m3, 16) || !aligned(x_bf16, 16) || !aligned(row_scale, 4) ||
+        !aligned(out_bf16, 2))
+        return QHEAD_ERR_ALIGN;
+    DeviceInfo dev;
+    if (int st = device_or_error(&dev)) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int32_t done = 0; done < rows;) {
+        const int32_t m = (rows - done) < 16 ? (rows - done) : 16;
+        hipError_t e = run_fp8_w8a16(w_e4m3, row_scale, x_bf16 + (size_t)done * hidden, m, hidden,
+                                     vocab, out_bf16 + (size_t)done * vocab, dev, s);
+        if (e != hipSuccess) return QHEAD_ERR_HIP;
+        done += m;
+    }
+    return QHEAD_OK;
+}
+
+int qhead_quant_act_e4m3(const uint16_t* x_bf16, int32_t rows, int32_t hidden, uint8_t* xq,
+                         float* xscale, void* stream) {
+    if (rows < 0 || hidden <= 0 || hidden % 16) return QHEAD_ERR_SHAPE;
+    if (rows == 0) return QHEAD_OK;
+    if (!x_bf16 || !xq || !xscale) return QHEAD_ERR_NULL;
+    if (!aligned(x_bf16, 16) || !aligned(xq, 8) || !aligned(xscale, 4)) return QHEAD_ERR_ALIGN;
+    DeviceInfo dev;
+    if (int st = device_or_error(&dev)) return st;
+    return hip_status(run_quant_act_e4m3(x_bf16, rows, hidden, xq, xscale,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+size_t qhead_w8a8_workspace_bytes(int32_t hidden) {
+    if (hidden <= 0) return 0;
+    return align256((size_t)128 * hidden) + align256(128 * sizeof(float));
+}
+
+int qhead_w8a8_gemv(const uint8_t* w_e4m3, const float* row_scale, const uint8_t* xq,
+                    const float* xscale, int32_t rows, int32_t hidden, int32_t vocab,
+                    uint16_t* out_bf16, void* stream) {
+    if (rows < 0 || hidden <= 0 || vocab <= 0 || hidden % 16) return QHEAD_ERR_SHAPE;
+    if (rows == 0) return QHEAD_OK;
+    if (!w_e4m3 || !row_scale || !xq || !xscale || !out_bf16) return QHEAD_ERR_NULL;
+    if (!aligned(w_e4m3, 16) || !aligned(xq, 8) || !aligned(row_scale, 4) ||
+        !aligned(xscale, 4) || !aligned(out_bf16, 2))
+        return QHEAD_ERR_ALIGN;
+    DeviceInfo dev;
+    if (int st = device_or_error(&dev)) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int32_t done = 0; done < rows;) {
+        const int32_t m = (rows - done) < kW8A8GemvRows ? (rows - done) : kW8A8GemvRows;
+        hipError_t e = run_fp8_w8a8(w_e4m3, row_scale, xq + (size_t)done * hidden, xscale + done,
+                                    m, hidden, vocab, out_bf16 + (size_t)done * vocab, dev, s);
+        if (e != hipSuccess) return QHEAD_ERR_HIP;
+        done += m;
+    }
+    return QHEAD_OK;
+}
+
+int qhead_w8a8(const uint8_t* w_e4m3, const float* row_scale, const uint16_t* x_bf16,
+               int32_t rows, int32_t hidden, int32_t vocab, uint16_t* out_bf16, void* workspace,
+               size_t workspace_bytes, void* stream) {
+    if (rows < 0 || hidden <= 0 || vocab <= 0 || hidden % 16) return QHEAD_ERR_SHAPE;
+    if (rows == 0) return QHEAD_OK;
+    if (!w_e4m3 || !row_scale || !x_bf16 || !out_bf16) return QHEAD_ERR_NULL;
+    if (!aligned(w_e4m3, 16) || !aligned(x_bf16, 16) || !aligned(row_scale, 4) ||
+        !aligned(out_bf16, 2))
+        return QHEAD_ERR_ALIGN;
+    if (!workspace || workspace_bytes < qhead_w8a8_workspace_bytes(hidden))
+        return QHEAD_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return QHEAD_ERR_ALIGN;
+    DeviceInfo dev;
+    if (int st = device_or_error(&dev)) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* xq = static_cast<uint8_t*>(workspace);
+    float* sa = reinterpret_cast<float*>(xq + align256((size_t)128 * hidden));
+    for (int32_t done = 0; done < rows;) {
+        const int32_t m = (rows - done) < 128 ? (rows - done) : 128;
+        hipError_t e = run_quant_act_e4m3(x_bf16 + (size_t)done * hidden, m, hidden, xq, sa, s);
+        if (e != hipSuccess) return QHEAD_ERR_HIP;
+        for (int32_t g = 0; g < m;) {
+            const int32_t gm = (m - g) < kW8A8GemvRows ? (m - g) : kW8A8GemvRows;
+            e = run_fp8_w8a8(w_e4m3, row_scale, xq + (size_t)g * hidden, sa + g, gm, hidden, vocab,
+                             out_bf16 + (size_t)(done + g) * vocab, dev, s);
+            if (e != hipSuccess) return QHEAD_ERR_HIP;
+            g += gm;
+        }
+        done += m;
+    }
+    return QHEAD_OK;
+}
+
+int qhead_nvfp4(const uint8_t* w_packed, const uint8_t* block_scale, const uint16_t* x_bf16,
+                int32_t rows, int32_t hidden, int32_t vocab, uint16_t* out_bf16,
+                float global_scale, void* stream) {
+    if (rows < 0 || hidden <= 0 || vocab <= 0 || hidden % 32) return QHEAD_ERR_SHAPE;
+    if (rows == 0) return QHEAD_OK;
+    if (!w_packed || !block_scale || !x_bf16 || !out_bf16) return QHEAD_ERR_NULL;
+    if (!aligned(w_packed, 16) || !aligned(block_scale, 2) || !aligned(x_bf16, 16) ||
+        !aligned(out_bf16, 2))
+        return QHEAD_ERR_ALIGN;
+    DeviceInfo dev;
+    if (int st = device_or_error(&dev)) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int32_t done = 0; done < rows;) {
+        const int32_t m = (rows - done) < 8 ? (rows - done) : 8;
+        hipError_t e = run_nvfp4(w_packed, block_scale, x_bf16 + (size_t)done * hidden,
+                                 global_scale, m, hidden, vocab,
+                                 out_bf16 + (size_t)done * vocab, dev, s);
+        if (e != hipSuccess) return QHEAD_ERR_HIP;
+        done += m;
+    }
+    return QHEAD_OK;
+}
+
+int qhead_quant_q8_1(const uint16_t* x_bf16, int32_t rows, int32_t hidden, void* q8_out,
+                     void* stream) {
+    if (rows < 0 || hidden <= 0 || hidden % 32) return QHEAD_ERR_SHAPE;
+    if (rows == 0) return QHEAD_OK;
+    if (!x_bf16 || !q8_out) return QHEAD_ERR_NULL;
+    if (!aligned(x_bf16, 16) || !aligned(q8_out, 4)) return QHEAD_ERR_ALIGN;
+    DeviceInfo dev;
+    if (int st = device_or_error(&dev)) return st;
+    return hip_status(run_quant_q8_1(x_bf16, rows, hidden, static_cast<uint8_t*>(q8_out),
+                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t qhead_q6k_workspace_bytes(int32_t hidden) {
+    if (hidden <= 0) return 0;
+    return align256((size_t)8 * (hidden / 32) * kQ8BlockBytes);
+}
+
+int qhead_q6k_gemv(const uint8_t* blocks, const void* q8, int32_t rows, int32_t hidden,
+                   int32_t vocab, uint16_t* out_bf16, void* stream) {
+    if (rows < 0 || hidden <= 0 || vocab <= 0 || hidden % 256) return QHEAD_ERR_SHAPE;
+    if (rows == 0) return QHEAD_OK;
+    if (!blocks || !q8 || !out_bf16) return QHEAD_ERR_NULL;
+    if (!aligned(blocks, 2) || !aligned(q8, 4) || !aligned(out_bf16, 2)) return QHEAD_ERR_ALIGN;
+    DeviceInfo dev;
+    if (int st = device_or_error(&dev)) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t q8_row = (size_t)(hidden / 32) * kQ8BlockBytes;
+    for (int32_t done = 0; done < rows;) {
+        const int32_t m = (rows - done) < 8 ? (rows - done) : 8;
+        hipError_t e = run_q6k(blocks, static_cast<const uint8_t*>(q8) + (size_t)done * q8_row, m,
+                               hidden, vocab, out_bf16 + (size_t)done * vocab, dev, s);
+        if (e != hipSuccess) return QHEAD_ERR_HIP;
+        done += m;
+    }
+    return QHEAD_OK;
+}
+
+int qhead_q6k(const uint8_t* blocks, const void* scales, const uint16_t* x_bf16, int32_t rows,
+              int32_t hidden, int32_t vocab, uint16_t* out_bf16, void* workspace,
+              size_t workspace_bytes, void* stream) {
+    if (scales != nullptr) return QHEAD_ERR_ARG;
+    if (rows < 0 || hidden <= 0 || vocab <= 0 || hidden % 256) return QHEAD_ERR_SHAPE;
+    if (rows == 0) return QHEAD_OK;
+    if (!blocks || !x_bf16 || !out_bf16) return QHEAD_ERR_NULL;
+    if (!aligned(blocks, 2) || !aligned(x_bf16, 16) || !aligned(out_bf16, 2))
+        return QHEAD_ERR_ALIGN;
+    if (!workspace || workspace_bytes < qhead_q6k_workspace_bytes(hidden))
+        return QHEAD_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return QHEAD_ERR_ALIGN;
+    DeviceInfo dev;
+    if (int st = device_or_error(&dev)) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* q8 = static_cast<uint8_t*>(workspace);
+    for (int32_t done = 0; done < rows;) {
+        const int32_t m = (rows - done) < 8 ? (rows - done) : 8;
+        hipError_t e = run_quant_q8_1(x_bf16 + (size_t)done * hidden, m, hidden, q8, s);
+        if (e != hipSuccess) return QHEAD_ERR_HIP;
+        e = run_q6k(blocks, q8, m, hidden, vocab, out_bf16 + (size_t)done * vocab, dev, s);
+        if (e != hipSuccess) return QHEAD_ERR_HIP;
+        done += m;
+    }
+    return QHEAD_OK;
+}
+
+int qhead_quantize_fp8_rows(const float* w_f32, int32_t vocab, int32_t hidden, uint8_t* w_e4m3,
+                            float* row_scale, void* stream) {
+    if (hidden <= 0 || vocab < 0 || hidden % 16) return QHEAD_ERR_SHAPE;
+    if (vocab == 0) return QHEAD_OK;
+    if (!w_f32 || !w_e4m3 || !row_scale) return QHEAD_ERR_NULL;
+    if (!aligned(w_f32, 16) || !aligned(w_e4m3, 4) || !aligned(row_scale, 4))
+        return QHEAD_ERR_ALIGN;
+    DeviceInfo dev;
+    if (int st = device_or_error(&dev)) return st;
+    return hip_status(run_quantize_fp8_rows(w_f32, vocab, hidden, w_e4m3, row_scale,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

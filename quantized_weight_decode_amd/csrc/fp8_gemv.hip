@@ -1,0 +1,296 @@
+// fp8_gemv.hip -- FP8 E4M3 head GEMV for 1..16 activation rows on gfx950.
+//
+// Computes logits[r][v] = bf16(fl32(acc * scale)) with acc = sum_k x[r][k] *
+// e4m3(W[v][k]) in FP32, for the FP8 head with one F32 scale per weight row
+// ("lm_head_fp8_rows.rs": module doc and lm_head_fp8_run, W8A16), and the
+// W8A8 variant that reads the same E4M3 bytes with E4M3 activations and a
+// per-row activation scale ("lm_head_fp8_rows.rs" set_lm_head_w8a8;
+// "w8a8_layer.rs" W8a8Ctx::proj).
+//
+// Design (MI355X-first; the pages' per-row-count kernels are prior art only):
+//  * One persistent workgroup of WAVES wave64s per CU. The activation rows are
+//    staged once per K-tile into LDS as BF16 (E4M3 activations are decoded to
+//    BF16 exactly while staging), so the weight stream is the only HBM
+//    traffic that scales with vocab.
+//  * Each wave owns bands of T consecutive vocab rows. A band's row is read as
+//    1 KiB segments: lane l loads bytes [16 l, 16 l + 16) of the segment, a
+//    coalesced 16-byte non-temporal load, so every weight byte is fetched
+//    exactly once per launch.
+//  * The 16 weights a lane holds are decoded to BF16 pairs in registers
+//    (v_cvt_scalef32_pk_bf16_fp8) and multiplied into FP32 accumulators with
+//    v_dot2_f32_bf16 against the lane's 16 activations of each row, read from
+//    LDS as two conflict-free 16-byte vectors.
+//  * After a K-tile, the T*R accumulators of the band are summed over the 64
+//    lanes by one fixed reduce-scatter tree (permlane swaps + DPP), then the
+//    tile sums are added in tile order, scaled, rounded to BF16 and stored.
+//
+// Row invariance: lane->k mapping, per-lane accumulation order (segments in
+// order, eight dot2 in k order), the cross-lane tree and the tile order all
+// depend on hidden only, never on R, T or the launch shape, so a row's logits
+// are bit-identical for every row count and every chunking.
+#include "qhead_device.h"
+#include "qhead_internal.h"
+
+namespace qh {
+
+constexpr int kSegK = 1024;        // k per wave segment: 64 lanes x 16
+constexpr int kTileK = 4096;       // k per LDS tile (fixed: part of the arithmetic)
+constexpr int kSegPerTile = kTileK / kSegK;
+constexpr int kVecPerTileRow = kTileK / 8;  // uint4 (8 BF16) per activation row per tile
+
+// LDS position (in uint4 units) of activations k_rel .. k_rel+7 within a
+// tile row: segment s, lane l, half c (k 16l..16l+7 -> c=0, 16l+8.. -> c=1),
+// laid out so that lanes read consecutive 16-byte vectors.
+__device__ __forceinline__ int lds_vec_index(int k_rel) {
+    const int s = k_rel >> 10;
+    const int w = k_rel & 1023;
+    const int l = w >> 4;
+    const int c = (w >> 3) & 1;
+    return s * 128 + c * 64 + l;
+}
+
+template <int R, bool W8A8, int NTHREADS>
+__device__ __forceinline__ void stage_tile(uint4* xs, const void* xin, int H, int k0, int nseg) {
+    const int vec_per_row = nseg * (kSegK / 8);
+    const int total = R * vec_per_row;
+    for (int idx = threadIdx.x; idx < total; idx += NTHREADS) {
+        const int r = idx / vec_per_row;
+        const int q = idx - r * vec_per_row;
+        const int k = k0 + q * 8;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (k < H) {
+            if constexpr (W8A8) {
+                const uint2 codes = *reinterpret_cast<const uint2*>(
+                    static_cast<const uint8_t*>(xin) + (size_t)r * H + k);
+                e4m3x4_to_bf16(codes.x, val.x, val.y);
+                e4m3x4_to_bf16(codes.y, val.z, val.w);
+            } else {
+                val = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xin) +
+                                                      (size_t)r * H + k);
+            }
+        }
+        xs[r * kVecPerTileRow + lds_vec_index(q * 8)] = val;
+    }
+}
+
+template <int R, int T, int WAVES, int MAXB, bool W8A8>
+__global__ void __launch_bounds__(WAVES * kWave)
+fp8_gemv_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
+                const void* __restrict__ xin, const float* __restrict__ xscale, int H, int V,
+                uint16_t* __restrict__ out, int nsuper) {
+    constexpr int N = T * R;
+    constexpr int NP = next_pow2(N);
+    constexpr int M = Log2<NP>::value;
+    static_assert(NP <= 64, "T*R must be <= 64");
+    __shared__ uint4 xs[R * kVecPerTileRow];
+
+    const int lane = threadIdx.x & 63;
+    // wave-uniform: keeps the band loop and its prefetch on scalar branches
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int TW = gridDim.x * WAVES;
+    const int gw = blockIdx.x * WAVES + wave;
+    const int NB = (V + T - 1) / T;
+    const int NT = (H + kTileK - 1) / kTileK;
+
+    // The value index this lane holds after the reduction: idx = r * T + t.
+    const int my_idx = lane >> (6 - M);
+    const int my_r = my_idx / T;
+    const int my_t = my_idx - my_r * T;
+    const bool writer = ((lane & ((1 << (6 - M)) - 1)) == 0) && (my_idx < N);
+
+    for (int sj = 0; sj < nsuper; ++sj) {
+        float part[MAXB];
+#pragma unroll
+        for (int bi = 0; bi < MAXB; ++bi) part[bi] = 0.0f;
+
+        for (int tt = 0; tt < NT; ++tt) {
+            const int k0 = tt * kTileK;
+            const int klen = min(kTileK, H - k0);
+            const int nseg = (klen + kSegK - 1) / kSegK;
+            if (NT > 1 || sj == 0) {
+                __syncthreads();
+                stage_tile<R, W8A8, WAVES * kWave>(xs, xin, H, k0, nseg);
+                __syncthreads();
+            }
+            // This wave's bands in this super-iteration, walked as one flat
+            // list of (band, segment) items so that the next item's weights
+            // are always in flight while the current one is computed.
+            const int first = (sj * MAXB) * TW + gw;
+            const int nbb = first < NB ? min(MAXB, (NB - 1 - first) / TW + 1) : 0;
+            const int nitems = nbb * nseg;
+            // Loads are unconditional so that no branch forces the wait
+            // counter to drain: a lane past the hidden tail re-reads the
+            // row's last 16 bytes (finite weights times the zero activations
+            // staged there add nothing), and a row past the vocab tail
+            // re-reads the last row (its sums are never stored).
+            auto load_item = [&](int bi, int s, uint4(&dst)[T]) {
+                const int v0 = ((sj * MAXB + bi) * TW + gw) * T;
+                const int k = min(k0 + s * kSegK + lane * 16, H - 16);
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const int v = min(v0 + t, V - 1);
+                    dst[t] = load_stream16(W + (size_t)v * H + k);
+                }
+            };
+            float acc[NP];
+            int bi = 0, s = 0;
+            // One (band, segment) item: issue the loads of item `it + 1` into
+            // `nxt` (clamped, unconditional), then compute `cur`. Two named
+            // buffers alternate, so no copy waits on a load in flight.
+            auto step = [&](int it, const uint4(&cur)[T], uint4(&nxt)[T]) {
+                {
+                    const bool last = it + 1 >= nitems;
+                    const int nbi = last ? bi : ((s + 1 == nseg) ? bi + 1 : bi);
+                    const int ns = last ? s : ((s + 1 == nseg) ? 0 : s + 1);
+                    load_item(nbi, ns, nxt);
+                }
+                if (s == 0) {
+#pragma unroll
+                    for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
+                }
+                uint32_t wb[T][8];
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    e4m3x4_to_bf16(cur[t].x, wb[t][0], wb[t][1]);
+                    e4m3x4_to_bf16(cur[t].y, wb[t][2], wb[t][3]);
+                    e4m3x4_to_bf16(cur[t].z, wb[t][4], wb[t][5]);
+                    e4m3x4_to_bf16(cur[t].w, wb[t][6], wb[t][7]);
+                }
+                // Activation rows through a ring of LA + 1 buffers: the
+                // reads of row r + LA are issued before row r is computed.
+                constexpr int LA = R < 2 ? R : 2;
+                constexpr int NBUF = LA + 1;
+                const uint4* xrow = xs + s * 128 + lane;
+                uint4 xr[NBUF][2];
+#pragma unroll
+                for (int r = 0; r < LA; ++r) {
+                    xr[r][0] = xrow[r * kVecPerTileRow];
+                    xr[r][1] = xrow[r * kVecPerTileRow + 64];
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if (r + LA < R) {
+                        xr[(r + LA) % NBUF][0] = xrow[(r + LA) * kVecPerTileRow];
+                        xr[(r + LA) % NBUF][1] = xrow[(r + LA) * kVecPerTileRow + 64];
+                    }
+                    const uint4 xa = xr[r % NBUF][0], xb = xr[r % NBUF][1];
+                    const uint32_t xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+                    for (int t = 0; t < T; ++t) {
+                        float a = acc[r * T + t];
+#pragma unroll
+                        for (int p = 0; p < 8; ++p) a = dot2_bf16(xv[p], wb[t][p], a);
+                        acc[r * T + t] = a;
+                    }
+                }
+                if (s + 1 == nseg) {
+                    wave_reduce_scatter<NP>(acc, lane);
+                    // part[bi] (+)= the tile sum, with bi a run-time index into
+                    // a register array: select through an unrolled compare.
+#pragma unroll
+                    for (int j = 0; j < MAXB; ++j)
+                        if (j == bi) part[j] = (tt == 0) ? acc[0] : part[j] + acc[0];
+                    ++bi;
+                    s = 0;
+                } else {
+                    ++s;
+                }
+            };
+            uint4 bufA[T], bufB[T];
+            if (nitems > 0) load_item(0, 0, bufA);
+            int it = 0;
+#pragma unroll 1
+            for (; it + 1 < nitems; it += 2) {
+                step(it, bufA, bufB);
+                step(it + 1, bufB, bufA);
+            }
+            if (it < nitems) step(it, bufA, bufB);
+        }
+
+        // Scales for all bands first (independent loads, one wait), then the
+        // stores.
+        float scl[MAXB];
+#pragma unroll
+        for (int bi = 0; bi < MAXB; ++bi) {
+            const int v = min(((sj * MAXB + bi) * TW + gw) * T + my_t, V - 1);
+            scl[bi] = wscale[v];
+        }
+        const float xs_r = W8A8 ? xscale[my_r] : 1.0f;
+#pragma unroll
+        for (int bi = 0; bi < MAXB; ++bi) {
+            const int band = (sj * MAXB + bi) * TW + gw;
+            const int v = band * T + my_t;
+            if (writer && band < NB && v < V) {
+                float y;
+                if constexpr (W8A8)
+                    y = (part[bi] * xs_r) * scl[bi];
+                else
+                    y = part[bi] * scl[bi];
+                out[(size_t)my_r * V + v] = f32_to_bf16_rne(y);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- launch
+
+template <int R, int T, int WAVES, int MAXB, bool W8A8>
+static hipError_t launch_fp8(const uint8_t* W, const float* wscale, const void* x,
+                             const float* xscale, int H, int V, uint16_t* out,
+                             const DeviceInfo& dev, hipStream_t stream) {
+    const int64_t NB = (V + T - 1) / T;
+    int64_t blocks = (NB + WAVES - 1) / WAVES;
+    if (blocks > dev.num_cus) blocks = dev.num_cus;
+    const int64_t TW = blocks * WAVES;
+    const int64_t per_wave = (NB + TW - 1) / TW;
+    const int nsuper = (int)((per_wave + MAXB - 1) / MAXB);
+    hipLaunchKernelGGL((fp8_gemv_kernel<R, T, WAVES, MAXB, W8A8>), dim3((unsigned)blocks),
+                       dim3(WAVES * kWave), 0, stream, W, wscale, x, xscale, H, V, out, nsuper);
+    return hipGetLastError();
+}
+
+// Launch shapes per row count: T vocab rows per wave keep the per-lane
+// accumulators (T*R) and the 16-byte loads in flight (T per wave) within the
+// register budget of 16 waves per CU.
+template <bool W8A8>
+static hipError_t dispatch_fp8(int R, const uint8_t* W, const float* wscale, const void* x,
+                               const float* xscale, int H, int V, uint16_t* out,
+                               const DeviceInfo& dev, hipStream_t stream) {
+    switch (R) {
+#define QH_FP8_CASE(RR, TT, MB) \
+    case RR:                    \
+        return launch_fp8<RR, TT, 16, MB, W8A8>(W, wscale, x, xscale, H, V, out, dev, stream);
+        QH_FP8_CASE(1, 4, 12)
+        QH_FP8_CASE(2, 4, 12)
+        QH_FP8_CASE(3, 4, 12)
+        QH_FP8_CASE(4, 4, 12)
+        QH_FP8_CASE(5, 2, 20)
+        QH_FP8_CASE(6, 2, 20)
+        QH_FP8_CASE(7, 2, 20)
+        QH_FP8_CASE(8, 2, 20)
+        QH_FP8_CASE(9, 2, 20)
+        QH_FP8_CASE(10, 2, 20)
+        QH_FP8_CASE(11, 2, 20)
+        QH_FP8_CASE(12, 2, 20)
+        QH_FP8_CASE(13, 2, 20)
+        QH_FP8_CASE(14, 2, 20)
+        QH_FP8_CASE(15, 2, 20)
+        QH_FP8_CASE(16, 2, 20)
+#undef QH_FP8_CASE
+        default:
+            return hipErrorInvalidValue;
+    }
+}
+
+hipError_t run_fp8_w8a16(const uint8_t* W, const float* s, const uint16_t* x, int R, int H, int V,
+                         uint16_t* out, const DeviceInfo& dev, hipStream_t stream) {
+    return dispatch_fp8<false>(R, W, s, x, nullptr, H, V, out, dev, stream);
+}
+
+hipError_t run_fp8_w8a8(const uint8_t* W, const float* sw, const uint8_t* xq, const float* sa,
+                        int R, int H, int V, uint16_t* out, const DeviceInfo& dev,
+                        hipStream_t stream) {
+    return dispatch_fp8<true>(R, W, sw, xq, sa, H, V, out, dev, stream);
+}
+
+}  // namespace qh

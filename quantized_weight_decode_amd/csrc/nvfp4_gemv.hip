@@ -1,0 +1,209 @@
+// nvfp4_gemv.hip -- NVFP4 (W4A16) head GEMV for 1..8 activation rows on gfx950.
+//
+// out[r][v] = bf16( fl32( g * sum_b e4m3(bs[v][b]) * p_b ) ),
+// p_b = sum_{k in block b} x[r][k] * e2m1(nib(v,k)) in FP32,
+// with blocks of 16 consecutive k and nib(v,k) the low nibble of packed byte
+// k/2 for even k ("fp8_lut.rs": dequant_nvfp4_to_bf16's value E2M1 * E4M3
+// block scale * global multiplier, and the even-index-low-nibble order stated
+// for the dequant_nvfp4_bf16 kernel). The pages serve 4..8 rows with narrow
+// tiers ("w4a16_gemv_tiers.rs": W4A16_BATCHM_WIDTHS, select_tier); here every
+// row count 1..8 is its own instantiation, so no dead rows execute.
+//
+// Same structure as the FP8 kernel: persistent workgroups, BF16 activations
+// staged in LDS per 8192-wide K-tile, bands of T vocab rows per wave, each
+// lane streaming 16 packed bytes (32 weights, two scale blocks) per 2048-wide
+// segment with one coalesced non-temporal load plus a 2-byte block-scale
+// load. Nibbles become BF16 pairs with v_cvt_scalef32_pk_bf16_fp4 (exact),
+// block partials use v_dot2_f32_bf16, and each block partial is folded into
+// the row accumulator with one FMA by its decoded E4M3 block scale. The
+// cross-lane tree, tile order and per-lane order depend only on hidden, so
+// rows are bit-identical for every row count.
+#include "qhead_device.h"
+#include "qhead_internal.h"
+
+namespace qh {
+
+constexpr int kF4SegK = 2048;                    // k per segment: 64 lanes x 32
+constexpr int kF4TileK = 8192;                   // k per LDS tile
+constexpr int kF4VecPerTileRow = kF4TileK / 8;   // uint4 per activation row per tile
+
+// LDS uint4 index of activations k_rel .. k_rel+7 in a tile row: segment s,
+// lane l (k 32l .. 32l+31 of the segment), quarter c (8 k each).
+__device__ __forceinline__ int f4_lds_vec_index(int k_rel) {
+    const int s = k_rel >> 11;
+    const int w = k_rel & 2047;
+    return s * 256 + ((w >> 3) & 3) * 64 + (w >> 5);
+}
+
+template <int R, int NTHREADS>
+__device__ __forceinline__ void f4_stage_tile(uint4* xs, const uint16_t* x, int H, int k0,
+                                              int nseg) {
+    const int vec_per_row = nseg * (kF4SegK / 8);
+    const int total = R * vec_per_row;
+    for (int idx = threadIdx.x; idx < total; idx += NTHREADS) {
+        const int r = idx / vec_per_row;
+        const int q = idx - r * vec_per_row;
+        const int k = k0 + q * 8;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (k < H) val = *reinterpret_cast<const uint4*>(x + (size_t)r * H + k);
+        xs[r * kF4VecPerTileRow + f4_lds_vec_index(q * 8)] = val;
+    }
+}
+
+template <int R, int T, int WAVES, int MAXB>
+__global__ void __launch_bounds__(WAVES * kWave)
+nvfp4_gemv_kernel(const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ bs,
+                  const uint16_t* __restrict__ x, float g, int H, int V,
+                  uint16_t* __restrict__ out, int nsuper) {
+    constexpr int N = T * R;
+    constexpr int NP = next_pow2(N);
+    constexpr int M = Log2<NP>::value;
+    static_assert(NP <= 64, "T*R must be <= 64");
+    __shared__ uint4 xs[R * kF4VecPerTileRow];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int TW = gridDim.x * WAVES;
+    const int gw = blockIdx.x * WAVES + wave;
+    const int NB = (V + T - 1) / T;
+    const int NT = (H + kF4TileK - 1) / kF4TileK;
+    const size_t prow = (size_t)H / 2;   // packed bytes per vocab row
+    const size_t brow = (size_t)H / 16;  // block scales per vocab row
+
+    const int my_idx = lane >> (6 - M);
+    const int my_r = my_idx / T;
+    const int my_t = my_idx - my_r * T;
+    const bool writer = ((lane & ((1 << (6 - M)) - 1)) == 0) && (my_idx < N);
+
+    for (int sj = 0; sj < nsuper; ++sj) {
+        float part[MAXB];
+#pragma unroll
+        for (int bi = 0; bi < MAXB; ++bi) part[bi] = 0.0f;
+
+        for (int tt = 0; tt < NT; ++tt) {
+            const int k0 = tt * kF4TileK;
+            const int klen = min(kF4TileK, H - k0);
+            const int nseg = (klen + kF4SegK - 1) / kF4SegK;
+            if (NT > 1 || sj == 0) {
+                __syncthreads();
+                f4_stage_tile<R, WAVES * kWave>(xs, x, H, k0, nseg);
+                __syncthreads();
+            }
+#pragma unroll 1
+            for (int bi = 0; bi < MAXB; ++bi) {
+                const int band = (sj * MAXB + bi) * TW + gw;
+                if (band >= NB) break;
+                const int v0 = band * T;
+                float acc[NP];
+#pragma unroll
+                for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
+
+                for (int s = 0; s < nseg; ++s) {
+                    const int k = k0 + s * kF4SegK + lane * 32;
+                    const bool kin = k < H;
+                    uint4 wr[T];
+                    uint32_t sc2[T];
+#pragma unroll
+                    for (int t = 0; t < T; ++t) {
+                        wr[t] = make_uint4(0, 0, 0, 0);
+                        sc2[t] = 0;
+                        if (v0 + t < V && kin) {
+                            wr[t] = load_stream16(Wp + (size_t)(v0 + t) * prow + (k >> 1));
+                            sc2[t] = *reinterpret_cast<const uint16_t*>(
+                                bs + (size_t)(v0 + t) * brow + (k >> 4));
+                        }
+                    }
+                    uint32_t wb[T][16];
+                    float bsf[T][2];
+#pragma unroll
+                    for (int t = 0; t < T; ++t) {
+                        const uint32_t d[4] = {wr[t].x, wr[t].y, wr[t].z, wr[t].w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            wb[t][4 * i + 0] = e2m1x2_to_bf16<0>(d[i]);
+                            wb[t][4 * i + 1] = e2m1x2_to_bf16<1>(d[i]);
+                            wb[t][4 * i + 2] = e2m1x2_to_bf16<2>(d[i]);
+                            wb[t][4 * i + 3] = e2m1x2_to_bf16<3>(d[i]);
+                        }
+                        bsf[t][0] = __builtin_amdgcn_cvt_f32_fp8(sc2[t], 0);
+                        bsf[t][1] = __builtin_amdgcn_cvt_f32_fp8(sc2[t], 1);
+                    }
+                    const int xbase = s * 256 + lane;
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        uint32_t xv[16];
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const uint4 q = xs[r * kF4VecPerTileRow + xbase + 64 * c];
+                            xv[4 * c + 0] = q.x;
+                            xv[4 * c + 1] = q.y;
+                            xv[4 * c + 2] = q.z;
+                            xv[4 * c + 3] = q.w;
+                        }
+#pragma unroll
+                        for (int t = 0; t < T; ++t) {
+                            float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+                            for (int p = 0; p < 8; ++p) p0 = dot2_bf16(xv[p], wb[t][p], p0);
+#pragma unroll
+                            for (int p = 8; p < 16; ++p) p1 = dot2_bf16(xv[p], wb[t][p], p1);
+                            float a = acc[r * T + t];
+                            a = __builtin_fmaf(bsf[t][0], p0, a);
+                            a = __builtin_fmaf(bsf[t][1], p1, a);
+                            acc[r * T + t] = a;
+                        }
+                    }
+                }
+                wave_reduce_scatter<NP>(acc, lane);
+#pragma unroll
+                for (int j = 0; j < MAXB; ++j)
+                    if (j == bi) part[j] = (tt == 0) ? acc[0] : part[j] + acc[0];
+            }
+        }
+
+#pragma unroll
+        for (int bi = 0; bi < MAXB; ++bi) {
+            const int band = (sj * MAXB + bi) * TW + gw;
+            if (band >= NB) break;
+            const int v = band * T + my_t;
+            if (writer && v < V) out[(size_t)my_r * V + v] = f32_to_bf16_rne(g * part[bi]);
+        }
+    }
+}
+
+template <int R, int T, int WAVES, int MAXB>
+static hipError_t launch_nvfp4(const uint8_t* Wp, const uint8_t* bs, const uint16_t* x, float g,
+                               int H, int V, uint16_t* out, const DeviceInfo& dev,
+                               hipStream_t stream) {
+    const int64_t NB = (V + T - 1) / T;
+    int64_t blocks = (NB + WAVES - 1) / WAVES;
+    if (blocks > dev.num_cus) blocks = dev.num_cus;
+    const int64_t TW = blocks * WAVES;
+    const int64_t per_wave = (NB + TW - 1) / TW;
+    const int nsuper = (int)((per_wave + MAXB - 1) / MAXB);
+    hipLaunchKernelGGL((nvfp4_gemv_kernel<R, T, WAVES, MAXB>), dim3((unsigned)blocks),
+                       dim3(WAVES * kWave), 0, stream, Wp, bs, x, g, H, V, out, nsuper);
+    return hipGetLastError();
+}
+
+hipError_t run_nvfp4(const uint8_t* Wp, const uint8_t* bs, const uint16_t* x, float g, int R,
+                     int H, int V, uint16_t* out, const DeviceInfo& dev, hipStream_t stream) {
+    switch (R) {
+#define QH_F4_CASE(RR, TT, MB) \
+    case RR:                   \
+        return launch_nvfp4<RR, TT, 16, MB>(Wp, bs, x, g, H, V, out, dev, stream);
+        QH_F4_CASE(1, 4, 12)
+        QH_F4_CASE(2, 4, 12)
+        QH_F4_CASE(3, 4, 12)
+        QH_F4_CASE(4, 4, 12)
+        QH_F4_CASE(5, 2, 20)
+        QH_F4_CASE(6, 2, 20)
+        QH_F4_CASE(7, 2, 20)
+        QH_F4_CASE(8, 2, 20)
+#undef QH_F4_CASE
+        default:
+            return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qh

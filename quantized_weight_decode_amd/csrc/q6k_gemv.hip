@@ -1,0 +1,239 @@
+// q6k_gemv.hip -- Q6_K x q8_1 head GEMV for 1..8 activation rows on gfx950.
+//
+// The head is held as raw 210-byte Q6_K super-blocks of 256 weights
+// ("lm_head_q6k.rs": LmHeadQ6k blocks [vocab][hidden/256], MAX_M = 8 rows
+// per kquant_mmvq launch) and the activations as block_q8_1 of 32 values
+// written by quant_q8_1. A weight is d * sc[t] * (q - 32) with q six bits
+// (low four in ql, high two in qh), sc an int8 per 16 weights and d fp16;
+// the byte placement follows the public GGUF description (ql[128] | qh[64] |
+// scales[16] | d):
+//   weight i = 128 n + 32 c + l:  ql[64 n + 32 (c & 1) + l], low nibble for
+//   c < 2, high for c >= 2; qh[32 n + l] bits 2c..2c+1.
+//
+// out[r][v] = bf16( sum over sub-blocks t of fl32(sc_t * isum_t) * fl32(d * d8_j) )
+// with isum_t = sum_{i in t} (q_i - 32) * q8_i an exact int32 (v_dot4_i32_i8)
+// and j the q8_1 block holding sub-block t; FP32 accumulation otherwise.
+//
+// Mapping (MI355X-first): 16 lanes per super-block, lane t of the 16 owns
+// sub-block t = the 16 consecutive weights 16t .. 16t+15, whose low bits are
+// 16 consecutive ql bytes and whose high bits are 16 consecutive qh bytes. A
+// wave covers four super-blocks (1024 weights) per segment. Super-blocks are
+// only 2-byte aligned (210 bytes), so each 16-byte field is read as five
+// aligned dwords and realigned with v_alignbyte (the extra dword stays
+// inside the super-block). The -32 offset is folded into the integer dot:
+// the staging step stores -32 * sum(q8) per sub-block next to the q8 values.
+#include "qhead_device.h"
+#include "qhead_internal.h"
+
+namespace qh {
+
+constexpr int kQSegK = 1024;                 // 4 super-blocks per wave segment
+constexpr int kQTileK = 8192;                // k per LDS tile (32 super-blocks)
+constexpr int kQSbPerTile = kQTileK / 256;
+
+struct Q6Lds {
+    int8_t q[8][kQTileK];               // q8 values [row][k]
+    float d8[8][kQTileK / 32];          // fp16 d of each q8 block, as f32
+    int32_t off[8][kQTileK / 16];       // -32 * sum of q8 over each 16-value sub-block
+};
+
+template <int R, int NTHREADS>
+__device__ __forceinline__ void q6_stage_tile(Q6Lds& L, const uint8_t* q8, int H, int k0,
+                                              int klen) {
+    const int nb = H / 32;
+    const int jb0 = k0 / 32;
+    const int nbt = klen / 32;  // q8 blocks in this tile
+    for (int idx = threadIdx.x; idx < R * nbt; idx += NTHREADS) {
+        const int r = idx / nbt;
+        const int j = idx - r * nbt;
+        const uint32_t* src =
+            reinterpret_cast<const uint32_t*>(q8 + ((size_t)r * nb + jb0 + j) * kQ8BlockBytes);
+        const uint32_t head = src[0];
+        const _Float16 d16 = __builtin_bit_cast(_Float16, (uint16_t)(head & 0xFFFFu));
+        L.d8[r][j] = (float)d16;
+        int s0 = 0, s1 = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t w = src[1 + i];
+            *reinterpret_cast<uint32_t*>(&L.q[r][j * 32 + 4 * i]) = w;
+            const int sum4 = __builtin_amdgcn_sdot4((int)w, 0x01010101, 0, false);
+            if (i < 4) s0 += sum4;
+            else s1 += sum4;
+        }
+        L.off[r][2 * j] = -32 * s0;
+        L.off[r][2 * j + 1] = -32 * s1;
+    }
+}
+
+// Sixteen bytes at a 2-byte-aligned address inside a super-block, read as
+// five aligned dwords (the fifth never leaves the super-block) and realigned.
+__device__ __forceinline__ void load16_a2(const uint8_t* p, uint32_t (&o)[4]) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3);
+    const uint32_t sh = (uint32_t)(a & 3);
+    uint32_t d[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) d[i] = __builtin_nontemporal_load(q + i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = __builtin_amdgcn_alignbyte(d[i + 1], d[i], sh);
+}
+
+template <int R, int T, int WAVES, int MAXB>
+__global__ void __launch_bounds__(WAVES * kWave)
+q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ q8, int H, int V,
+                uint16_t* __restrict__ out, int nsuper) {
+    constexpr int N = T * R;
+    constexpr int NP = next_pow2(N);
+    constexpr int M = Log2<NP>::value;
+    static_assert(NP <= 64 && R <= 8, "T*R must be <= 64, R <= 8");
+    __shared__ Q6Lds L;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int TW = gridDim.x * WAVES;
+    const int gw = blockIdx.x * WAVES + wave;
+    const int NB = (V + T - 1) / T;
+    const int NT = (H + kQTileK - 1) / kQTileK;
+    const int nsb = H / 256;
+    const size_t rowbytes = (size_t)nsb * kQ6KBlockBytes;
+
+    // lane -> (super-block within the segment, sub-block t = 8n + 2c + h)
+    const int sbi = lane >> 4;
+    const int t16 = lane & 15;
+    const int n = t16 >> 3, c = (t16 >> 1) & 3, h = t16 & 1;
+    const int ql_off = 64 * n + 32 * (c & 1) + 16 * h;
+    const int qh_off = 128 + 32 * n + 16 * h;
+    const int lo_shift = (c >= 2) ? 4 : 0;
+    const int hi_shift = 2 * c;
+
+    const int my_idx = lane >> (6 - M);
+    const int my_r = my_idx / T;
+    const int my_t = my_idx - my_r * T;
+    const bool writer = ((lane & ((1 << (6 - M)) - 1)) == 0) && (my_idx < N);
+
+    for (int sj = 0; sj < nsuper; ++sj) {
+        float part[MAXB];
+#pragma unroll
+        for (int bi = 0; bi < MAXB; ++bi) part[bi] = 0.0f;
+
+        for (int tt = 0; tt < NT; ++tt) {
+            const int k0 = tt * kQTileK;
+            const int klen = min(kQTileK, H - k0);
+            const int nsb_tile = klen / 256;
+            const int nseg = (nsb_tile + 3) / 4;
+            if (NT > 1 || sj == 0) {
+                __syncthreads();
+                q6_stage_tile<R, WAVES * kWave>(L, q8, H, k0, klen);
+                __syncthreads();
+            }
+#pragma unroll 1
+            for (int bi = 0; bi < MAXB; ++bi) {
+                const int band = (sj * MAXB + bi) * TW + gw;
+                if (band >= NB) break;
+                const int v0 = band * T;
+                float acc[NP];
+#pragma unroll
+                for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
+
+                for (int s = 0; s < nseg; ++s) {
+                    const int sbt = s * 4 + sbi;          // super-block within the tile
+                    const bool sin = sbt < nsb_tile;
+                    const int sb = tt * kQSbPerTile + sbt;  // super-block within the row
+                    uint32_t qw[T][4];
+                    float dsc[T];
+                    int scv[T];
+#pragma unroll
+                    for (int t = 0; t < T; ++t) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) qw[t][i] = 0;
+                        dsc[t] = 0.0f;
+                        scv[t] = 0;
+                        if (v0 + t < V && sin) {
+                            const uint8_t* blk = blocks + (size_t)(v0 + t) * rowbytes +
+                                                 (size_t)sb * kQ6KBlockBytes;
+                            uint32_t ql[4], qh[4];
+                            load16_a2(blk + ql_off, ql);
+                            load16_a2(blk + qh_off, qh);
+                            const uint16_t dbits = *reinterpret_cast<const uint16_t*>(blk + 208);
+                            dsc[t] = (float)__builtin_bit_cast(_Float16, dbits);
+                            scv[t] = (int)(int8_t)blk[192 + t16];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const uint32_t lo = (ql[i] >> lo_shift) & 0x0F0F0F0Fu;
+                                const uint32_t hi = ((qh[i] >> hi_shift) & 0x03030303u) << 4;
+                                qw[t][i] = lo | hi;
+                            }
+                        }
+                    }
+                    if (sin) {
+                        const int kk = sbt * 256 + 16 * t16;   // k within the tile
+                        const int jt = kk >> 5;                 // q8 block within the tile
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            const uint4 xq = *reinterpret_cast<const uint4*>(&L.q[r][kk]);
+                            const int off = L.off[r][kk >> 4];
+                            const float d8 = L.d8[r][jt];
+#pragma unroll
+                            for (int t = 0; t < T; ++t) {
+                                int is = __builtin_amdgcn_sdot4((int)qw[t][0], (int)xq.x, off, false);
+                                is = __builtin_amdgcn_sdot4((int)qw[t][1], (int)xq.y, is, false);
+                                is = __builtin_amdgcn_sdot4((int)qw[t][2], (int)xq.z, is, false);
+                                is = __builtin_amdgcn_sdot4((int)qw[t][3], (int)xq.w, is, false);
+                                const float f = (float)(is * scv[t]);
+                                acc[r * T + t] = __builtin_fmaf(f, dsc[t] * d8, acc[r * T + t]);
+                            }
+                        }
+                    }
+                }
+                wave_reduce_scatter<NP>(acc, lane);
+#pragma unroll
+                for (int j = 0; j < MAXB; ++j)
+                    if (j == bi) part[j] = (tt == 0) ? acc[0] : part[j] + acc[0];
+            }
+        }
+
+#pragma unroll
+        for (int bi = 0; bi < MAXB; ++bi) {
+            const int band = (sj * MAXB + bi) * TW + gw;
+            if (band >= NB) break;
+            const int v = band * T + my_t;
+            if (writer && v < V) out[(size_t)my_r * V + v] = f32_to_bf16_rne(part[bi]);
+        }
+    }
+}
+
+template <int R, int T, int WAVES, int MAXB>
+static hipError_t launch_q6k(const uint8_t* blocks, const uint8_t* q8, int H, int V,
+                             uint16_t* out, const DeviceInfo& dev, hipStream_t stream) {
+    const int64_t NB = (V + T - 1) / T;
+    int64_t nblk = (NB + WAVES - 1) / WAVES;
+    if (nblk > dev.num_cus) nblk = dev.num_cus;
+    const int64_t TW = nblk * WAVES;
+    const int64_t per_wave = (NB + TW - 1) / TW;
+    const int nsuper = (int)((per_wave + MAXB - 1) / MAXB);
+    hipLaunchKernelGGL((q6k_gemv_kernel<R, T, WAVES, MAXB>), dim3((unsigned)nblk),
+                       dim3(WAVES * kWave), 0, stream, blocks, q8, H, V, out, nsuper);
+    return hipGetLastError();
+}
+
+hipError_t run_q6k(const uint8_t* blocks, const uint8_t* q8, int R, int H, int V, uint16_t* out,
+                   const DeviceInfo& dev, hipStream_t stream) {
+    switch (R) {
+#define QH_Q6_CASE(RR, TT, MB) \
+    case RR:                   \
+        return launch_q6k<RR, TT, 16, MB>(blocks, q8, H, V, out, dev, stream);
+        QH_Q6_CASE(1, 4, 12)
+        QH_Q6_CASE(2, 4, 12)
+        QH_Q6_CASE(3, 4, 12)
+        QH_Q6_CASE(4, 4, 12)
+        QH_Q6_CASE(5, 2, 20)
+        QH_Q6_CASE(6, 2, 20)
+        QH_Q6_CASE(7, 2, 20)
+        QH_Q6_CASE(8, 2, 20)
+#undef QH_Q6_CASE
+        default:
+            return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qh

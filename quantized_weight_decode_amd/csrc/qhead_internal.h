@@ -1,0 +1,41 @@
+// qhead_internal.h -- host-side declarations shared by the libqhead sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qh {
+
+struct DeviceInfo {
+    int device = -1;
+    int num_cus = 0;
+    bool is_gfx950 = false;
+};
+
+// Attributes of the current device (cached per device id).
+hipError_t current_device(DeviceInfo* out);
+
+// FP8 family (1 <= R <= 16 rows per launch).
+hipError_t run_fp8_w8a16(const uint8_t* W, const float* s, const uint16_t* x, int R, int H, int V,
+                         uint16_t* out, const DeviceInfo& dev, hipStream_t stream);
+hipError_t run_fp8_w8a8(const uint8_t* W, const float* sw, const uint8_t* xq, const float* sa,
+                        int R, int H, int V, uint16_t* out, const DeviceInfo& dev,
+                        hipStream_t stream);
+
+// Activation quantizers and weight preparation.
+hipError_t run_quant_act_e4m3(const uint16_t* x, int rows, int H, uint8_t* xq, float* sa,
+                              hipStream_t stream);
+hipError_t run_quant_q8_1(const uint16_t* x, int rows, int H, uint8_t* q8, hipStream_t stream);
+hipError_t run_quantize_fp8_rows(const float* w, int V, int H, uint8_t* codes, float* scales,
+                                 hipStream_t stream);
+
+// NVFP4 (1 <= R <= 8) and Q6_K (1 <= R <= 8).
+hipError_t run_nvfp4(const uint8_t* Wp, const uint8_t* bs, const uint16_t* x, float g, int R,
+                     int H, int V, uint16_t* out, const DeviceInfo& dev, hipStream_t stream);
+hipError_t run_q6k(const uint8_t* blocks, const uint8_t* q8, int R, int H, int V, uint16_t* out,
+                   const DeviceInfo& dev, hipStream_t stream);
+
+constexpr int kQ8BlockBytes = 36;
+constexpr int kQ6KBlockBytes = 210;
+
+}  // namespace qh

@@ -1,0 +1,146 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/qhead.h declares, rejects invalid arguments before touching the
+device, and plans row chunks as the pages' chunk loops do (16 rows per FP8
+W8A16 pass, 128 per W8A8 call, 8 per NVFP4 / Q6_K pass)."""
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def qh():
+    lib = os.path.join(ROOT, "quantized_weight_decode_amd", "libqhead.so")
+    if not os.path.exists(lib):
+        subprocess.run(["python", os.path.join(ROOT, "quantized_weight_decode_amd", "build.py")],
+                       check=True)
+    import quantized_weight_decode_amd as m
+
+    return m
+
+
+# fake device addresses: never dereferenced, the calls return before any HIP call
+A16 = 0x10000
+A256 = 0x20000
+MIS = 0x10001
+
+
+def test_exports_every_declared_function(qh):
+    names = qh.header_functions()
+    assert len(names) == 14
+    for n in names:
+        assert hasattr(qh.lib(), n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", qh.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert set(names) <= exported
+
+
+def test_status_strings(qh):
+    for st in range(-7, 1):
+        assert qh.status_string(st) and qh.status_string(st) != "unknown status"
+    assert qh.status_string(-99) == "unknown status"
+
+
+def test_plan_chunks(qh):
+    assert qh.plan_chunks(qh.FMT_FP8, 40) == [16, 16, 8]
+    assert qh.plan_chunks(qh.FMT_FP8, 64) == [16, 16, 16, 16]
+    assert qh.plan_chunks(qh.FMT_FP8, 16) == [16]
+    assert qh.plan_chunks(qh.FMT_FP8, 1) == [1]
+    assert qh.plan_chunks(qh.FMT_W8A8, 300) == [128, 128, 44]
+    assert qh.plan_chunks(qh.FMT_W8A8, 128) == [128]
+    assert qh.plan_chunks(qh.FMT_NVFP4, 8) == [8]
+    assert qh.plan_chunks(qh.FMT_Q6K, 13) == [8, 5]
+    assert qh.plan_chunks(qh.FMT_Q6K, 0) == []
+    L = qh.lib()
+    assert L.qhead_plan_chunks(qh.FMT_FP8, -1, None, 0) == -2
+    assert L.qhead_plan_chunks(9, 4, None, 0) == -5
+    buf = (ctypes.c_int32 * 2)()
+    # a short buffer still returns the full count and fills what fits
+    assert L.qhead_plan_chunks(qh.FMT_FP8, 50, buf, 2) == 4
+    assert list(buf) == [16, 16]
+    assert [qh.max_rows_per_launch(f) for f in range(4)] == [16, 128, 8, 8]
+    assert L.qhead_max_rows_per_launch(7) == -5
+
+
+def test_workspace_sizes(qh):
+    assert qh.w8a8_workspace_bytes(7168) >= 128 * 7168 + 128 * 4
+    assert qh.w8a8_workspace_bytes(7168) % 256 == 0
+    assert qh.w8a8_workspace_bytes(0) == 0
+    assert qh.q6k_workspace_bytes(7168) >= 8 * (7168 // 32) * 36
+    assert qh.q6k_workspace_bytes(-5) == 0
+
+
+def test_fp8_validation(qh):
+    f = qh.lib().qhead_fp8_rowscale
+    assert f(None, A16, A16, 1, 16, 8, A16, None) == -1
+    assert f(A16, A16, A16, -1, 16, 8, A16, None) == -2
+    assert f(A16, A16, A16, 1, 24, 8, A16, None) == -2   # hidden % 16
+    assert f(A16, A16, A16, 1, 16, 0, A16, None) == -2
+    assert f(MIS, A16, A16, 1, 16, 8, A16, None) == -3
+    assert f(A16, A16, A16 + 8, 1, 16, 8, A16, None) == -3
+    assert f(A16, A16, A16, 1, 16, 8, MIS, None) == -3
+    assert f(A16, A16, A16, 0, 16, 8, A16, None) == 0     # rows = 0: no launch
+
+
+def test_w8a8_validation(qh):
+    L = qh.lib()
+    ws = qh.w8a8_workspace_bytes(64)
+    f = L.qhead_w8a8
+    assert f(A16, A16, A16, 1, 64, 8, A16, None, ws, None) == -4
+    assert f(A16, A16, A16, 1, 64, 8, A16, A256, ws - 1, None) == -4
+    assert f(A16, A16, A16, 1, 64, 8, A16, A256 + 16, ws, None) == -3
+    assert f(A16, A16, A16, 1, 65, 8, A16, A256, ws, None) == -2
+    assert f(A16, A16, A16, 0, 64, 8, A16, A256, ws, None) == 0
+    g = L.qhead_quant_act_e4m3
+    assert g(A16, 2, 64, None, A16, None) == -1
+    assert g(A16, 2, 64, A16 + 4, A16, None) == -3
+    assert g(A16, 0, 64, A16, A16, None) == 0
+    h = L.qhead_w8a8_gemv
+    assert h(A16, A16, A16, None, 1, 64, 8, A16, None) == -1
+    assert h(A16, A16, A16, A16, 0, 64, 8, A16, None) == 0
+
+
+def test_nvfp4_validation(qh):
+    f = qh.lib().qhead_nvfp4
+    assert f(A16, A16, A16, 1, 48, 8, A16, 1.0, None) == -2   # hidden % 32
+    assert f(A16, A16 + 1, A16, 1, 64, 8, A16, 1.0, None) == -3
+    assert f(A16, None, A16, 1, 64, 8, A16, 1.0, None) == -1
+    assert f(A16, A16, A16, 0, 64, 8, A16, 1.0, None) == 0
+
+
+def test_q6k_validation(qh):
+    L = qh.lib()
+    ws = qh.q6k_workspace_bytes(512)
+    f = L.qhead_q6k
+    assert f(A16, A16, A16, 1, 512, 8, A16, A256, ws, None) == -5   # scales must be NULL
+    assert f(A16, None, A16, 1, 384, 8, A16, A256, ws, None) == -2  # hidden % 256
+    assert f(A16, None, A16, 1, 512, 8, A16, A256, ws - 1, None) == -4
+    assert f(A16 + 1, None, A16, 1, 512, 8, A16, A256, ws, None) == -3
+    assert f(A16, None, A16, 0, 512, 8, A16, A256, ws, None) == 0
+    g = L.qhead_quant_q8_1
+    assert g(A16, 1, 48, A16, None) == -2
+    assert g(A16, 1, 64, A16 + 2, None) == -3
+    assert g(A16, 0, 64, A16, None) == 0
+    h = L.qhead_q6k_gemv
+    assert h(A16, A16 + 2, 1, 256, 8, A16, None) == -3
+    assert h(A16, A16, 0, 256, 8, A16, None) == 0
+
+
+def test_quantize_fp8_rows_validation(qh):
+    f = qh.lib().qhead_quantize_fp8_rows
+    assert f(A16, 8, 24, A16, A16, None) == -2
+    assert f(A16 + 4, 8, 16, A16, A16, None) == -3
+    assert f(A16, 0, 16, A16, A16, None) == 0
+
+
+def test_binding_rejects_host_tensors(qh):
+    import torch
+
+    w = torch.zeros((8, 16), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        qh.fp8_rowscale(w, torch.zeros(8), torch.zeros((1, 16), dtype=torch.bfloat16))
