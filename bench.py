@@ -31,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "fp8_gemv_cfg2_counters.json")
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "fp8_gemv_155136x8192_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_weight_decode_amd", "csrc", f)
                   for f in ("fp8_gemv.hip", "qhead_device.h")]
 
@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target duration of the oracle CPU baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only copy 1 GiB device to device (for rocprofv3 FETCH_SIZE/WRITE_SIZE "
+                         "calibration) and exit")
     return ap.parse_args()
 
 
@@ -130,6 +133,18 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        # A plain copy of known size: the counters of this one kernel give the
+        # factor between FETCH_SIZE / WRITE_SIZE readings and bytes moved.
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
+        return
 
     import quantized_weight_decode_amd as qh
 

@@ -35,7 +35,6 @@ namespace qh {
 
 constexpr int kSegK = 1024;        // k per wave segment: 64 lanes x 16
 constexpr int kTileK = 4096;       // k per LDS tile (fixed: part of the arithmetic)
-constexpr int kSegPerTile = kTileK / kSegK;
 constexpr int kVecPerTileRow = kTileK / 8;  // uint4 (8 BF16) per activation row per tile
 
 // LDS position (in uint4 units) of activations k_rel .. k_rel+7 within a
@@ -73,8 +72,8 @@ __device__ __forceinline__ void stage_tile(uint4* xs, const void* xin, int H, in
     }
 }
 
-template <int R, int T, int WAVES, int MAXB, bool W8A8>
-__global__ void __launch_bounds__(WAVES * kWave)
+template <int R, int T, int WAVES, int MAXB, int BPC, bool W8A8>
+__global__ void __launch_bounds__(WAVES * kWave, (WAVES * BPC + 3) / 4)
 fp8_gemv_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
                 const void* __restrict__ xin, const float* __restrict__ xscale, int H, int V,
                 uint16_t* __restrict__ out, int nsuper) {
@@ -234,48 +233,53 @@ fp8_gemv_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
 
 // ---------------------------------------------------------------- launch
 
-template <int R, int T, int WAVES, int MAXB, bool W8A8>
+// A launch shape: T vocab rows per wave, WAVES waves per workgroup, MAXB
+// bands per wave between activation restagings, BPC workgroups per CU.
+template <int R, int T, int WAVES, int MAXB, int BPC, bool W8A8>
 static hipError_t launch_fp8(const uint8_t* W, const float* wscale, const void* x,
                              const float* xscale, int H, int V, uint16_t* out,
                              const DeviceInfo& dev, hipStream_t stream) {
     const int64_t NB = (V + T - 1) / T;
     int64_t blocks = (NB + WAVES - 1) / WAVES;
-    if (blocks > dev.num_cus) blocks = dev.num_cus;
+    if (blocks > (int64_t)dev.num_cus * BPC) blocks = (int64_t)dev.num_cus * BPC;
     const int64_t TW = blocks * WAVES;
     const int64_t per_wave = (NB + TW - 1) / TW;
     const int nsuper = (int)((per_wave + MAXB - 1) / MAXB);
-    hipLaunchKernelGGL((fp8_gemv_kernel<R, T, WAVES, MAXB, W8A8>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((fp8_gemv_kernel<R, T, WAVES, MAXB, BPC, W8A8>), dim3((unsigned)blocks),
                        dim3(WAVES * kWave), 0, stream, W, wscale, x, xscale, H, V, out, nsuper);
     return hipGetLastError();
 }
 
-// Launch shapes per row count: T vocab rows per wave keep the per-lane
-// accumulators (T*R) and the 16-byte loads in flight (T per wave) within the
-// register budget of 16 waves per CU.
+// Launch shape per row count, chosen by timing the 155136 x 8192 head on
+// MI355X. Few rows are HBM-bound: many small workgroups keep more 16-byte
+// loads in flight. From 5 rows on the VALU bounds the kernel: wider bands (T)
+// cut LDS activation reads per weight byte (2R/T bytes) and 8-wave groups
+// leave room for T*R accumulators. The shape never changes a row's bits.
 template <bool W8A8>
 static hipError_t dispatch_fp8(int R, const uint8_t* W, const float* wscale, const void* x,
                                const float* xscale, int H, int V, uint16_t* out,
                                const DeviceInfo& dev, hipStream_t stream) {
     switch (R) {
-#define QH_FP8_CASE(RR, TT, MB) \
-    case RR:                    \
-        return launch_fp8<RR, TT, 16, MB, W8A8>(W, wscale, x, xscale, H, V, out, dev, stream);
-        QH_FP8_CASE(1, 4, 12)
-        QH_FP8_CASE(2, 4, 12)
-        QH_FP8_CASE(3, 4, 12)
-        QH_FP8_CASE(4, 4, 12)
-        QH_FP8_CASE(5, 2, 20)
-        QH_FP8_CASE(6, 2, 20)
-        QH_FP8_CASE(7, 2, 20)
-        QH_FP8_CASE(8, 2, 20)
-        QH_FP8_CASE(9, 2, 20)
-        QH_FP8_CASE(10, 2, 20)
-        QH_FP8_CASE(11, 2, 20)
-        QH_FP8_CASE(12, 2, 20)
-        QH_FP8_CASE(13, 2, 20)
-        QH_FP8_CASE(14, 2, 20)
-        QH_FP8_CASE(15, 2, 20)
-        QH_FP8_CASE(16, 2, 20)
+#define QH_FP8_CASE(RR, TT, WV, MB, BPC)                                                       \
+    case RR:                                                                                  \
+        return launch_fp8<RR, TT, WV, MB, BPC, W8A8>(W, wscale, x, xscale, H, V, out, dev, \
+                                                     stream);
+        QH_FP8_CASE(1, 2, 8, 12, 4)
+        QH_FP8_CASE(2, 4, 4, 12, 4)
+        QH_FP8_CASE(3, 4, 16, 12, 1)
+        QH_FP8_CASE(4, 4, 16, 12, 1)
+        QH_FP8_CASE(5, 8, 8, 12, 1)
+        QH_FP8_CASE(6, 8, 8, 12, 1)
+        QH_FP8_CASE(7, 8, 8, 12, 1)
+        QH_FP8_CASE(8, 8, 8, 12, 1)
+        QH_FP8_CASE(9, 4, 8, 20, 1)
+        QH_FP8_CASE(10, 4, 8, 20, 1)
+        QH_FP8_CASE(11, 4, 8, 20, 1)
+        QH_FP8_CASE(12, 4, 8, 20, 1)
+        QH_FP8_CASE(13, 4, 8, 20, 1)
+        QH_FP8_CASE(14, 4, 8, 20, 1)
+        QH_FP8_CASE(15, 4, 8, 20, 1)
+        QH_FP8_CASE(16, 4, 8, 20, 1)
 #undef QH_FP8_CASE
         default:
             return hipErrorInvalidValue;

@@ -50,8 +50,8 @@ __device__ __forceinline__ void f4_stage_tile(uint4* xs, const uint16_t* x, int 
     }
 }
 
-template <int R, int T, int WAVES, int MAXB>
-__global__ void __launch_bounds__(WAVES * kWave)
+template <int R, int T, int WAVES, int MAXB, int BPC>
+__global__ void __launch_bounds__(WAVES * kWave, (WAVES * BPC + 3) / 4)
 nvfp4_gemv_kernel(const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ bs,
                   const uint16_t* __restrict__ x, float g, int H, int V,
                   uint16_t* __restrict__ out, int nsuper) {
@@ -62,7 +62,7 @@ nvfp4_gemv_kernel(const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ bs
     __shared__ uint4 xs[R * kF4VecPerTileRow];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int TW = gridDim.x * WAVES;
     const int gw = blockIdx.x * WAVES + wave;
     const int NB = (V + T - 1) / T;
@@ -74,6 +74,11 @@ nvfp4_gemv_kernel(const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ bs
     const int my_r = my_idx / T;
     const int my_t = my_idx - my_r * T;
     const bool writer = ((lane & ((1 << (6 - M)) - 1)) == 0) && (my_idx < N);
+
+    struct Item {
+        uint4 w[T];
+        uint32_t sc[T];
+    };
 
     for (int sj = 0; sj < nsuper; ++sj) {
         float part[MAXB];
@@ -89,99 +94,170 @@ nvfp4_gemv_kernel(const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ bs
                 f4_stage_tile<R, WAVES * kWave>(xs, x, H, k0, nseg);
                 __syncthreads();
             }
-#pragma unroll 1
-            for (int bi = 0; bi < MAXB; ++bi) {
-                const int band = (sj * MAXB + bi) * TW + gw;
-                if (band >= NB) break;
-                const int v0 = band * T;
-                float acc[NP];
+            const int first = (sj * MAXB) * TW + gw;
+            const int nbb = first < NB ? min(MAXB, (NB - 1 - first) / TW + 1) : 0;
+            const int nitems = nbb * nseg;
+            // Unconditional loads: a lane past the hidden tail re-reads the
+            // row's last 32 weights (times zero activations), a row past the
+            // vocab tail re-reads the last row (never stored).
+            auto load_item = [&](int bi, int s, Item& dst) {
+                const int v0 = ((sj * MAXB + bi) * TW + gw) * T;
+                const int k = min(k0 + s * kF4SegK + lane * 32, H - 32);
 #pragma unroll
-                for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
-
-                for (int s = 0; s < nseg; ++s) {
-                    const int k = k0 + s * kF4SegK + lane * 32;
-                    const bool kin = k < H;
-                    uint4 wr[T];
-                    uint32_t sc2[T];
+                for (int t = 0; t < T; ++t) {
+                    const int v = min(v0 + t, V - 1);
+                    dst.w[t] = load_stream16(Wp + (size_t)v * prow + (k >> 1));
+                    dst.sc[t] = *reinterpret_cast<const uint16_t*>(bs + (size_t)v * brow + (k >> 4));
+                }
+            };
+            float acc[NP];
+            int bi = 0, s = 0;
+            auto step = [&](int it, const Item& cur, Item& nxt) {
+                {
+                    const bool last = it + 1 >= nitems;
+                    const int nbi = last ? bi : ((s + 1 == nseg) ? bi + 1 : bi);
+                    const int ns = last ? s : ((s + 1 == nseg) ? 0 : s + 1);
+                    load_item(nbi, ns, nxt);
+                }
+                if (s == 0) {
 #pragma unroll
-                    for (int t = 0; t < T; ++t) {
-                        wr[t] = make_uint4(0, 0, 0, 0);
-                        sc2[t] = 0;
-                        if (v0 + t < V && kin) {
-                            wr[t] = load_stream16(Wp + (size_t)(v0 + t) * prow + (k >> 1));
-                            sc2[t] = *reinterpret_cast<const uint16_t*>(
-                                bs + (size_t)(v0 + t) * brow + (k >> 4));
-                        }
-                    }
-                    uint32_t wb[T][16];
-                    float bsf[T][2];
-#pragma unroll
-                    for (int t = 0; t < T; ++t) {
-                        const uint32_t d[4] = {wr[t].x, wr[t].y, wr[t].z, wr[t].w};
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            wb[t][4 * i + 0] = e2m1x2_to_bf16<0>(d[i]);
-                            wb[t][4 * i + 1] = e2m1x2_to_bf16<1>(d[i]);
-                            wb[t][4 * i + 2] = e2m1x2_to_bf16<2>(d[i]);
-                            wb[t][4 * i + 3] = e2m1x2_to_bf16<3>(d[i]);
-                        }
-                        bsf[t][0] = __builtin_amdgcn_cvt_f32_fp8(sc2[t], 0);
-                        bsf[t][1] = __builtin_amdgcn_cvt_f32_fp8(sc2[t], 1);
-                    }
-                    const int xbase = s * 256 + lane;
+                    for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
+                }
+                const uint4* xrow = xs + s * 256 + lane;
+                if constexpr (R <= 2) {
+                    // Few rows: hold every row's 32 activations, decode one
+                    // vocab row's nibbles at a time (fewer live registers).
+                    uint32_t xv[R][16];
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
-                        uint32_t xv[16];
 #pragma unroll
                         for (int c = 0; c < 4; ++c) {
-                            const uint4 q = xs[r * kF4VecPerTileRow + xbase + 64 * c];
-                            xv[4 * c + 0] = q.x;
-                            xv[4 * c + 1] = q.y;
-                            xv[4 * c + 2] = q.z;
-                            xv[4 * c + 3] = q.w;
+                            const uint4 q = xrow[r * kF4VecPerTileRow + 64 * c];
+                            xv[r][4 * c + 0] = q.x;
+                            xv[r][4 * c + 1] = q.y;
+                            xv[r][4 * c + 2] = q.z;
+                            xv[r][4 * c + 3] = q.w;
                         }
+                    }
 #pragma unroll
-                        for (int t = 0; t < T; ++t) {
+                    for (int t = 0; t < T; ++t) {
+                        uint32_t wb[16];
+                        const uint32_t d[4] = {cur.w[t].x, cur.w[t].y, cur.w[t].z, cur.w[t].w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            wb[4 * i + 0] = e2m1x2_to_bf16<0>(d[i]);
+                            wb[4 * i + 1] = e2m1x2_to_bf16<1>(d[i]);
+                            wb[4 * i + 2] = e2m1x2_to_bf16<2>(d[i]);
+                            wb[4 * i + 3] = e2m1x2_to_bf16<3>(d[i]);
+                        }
+                        const float b0 = __builtin_amdgcn_cvt_f32_fp8(cur.sc[t], 0);
+                        const float b1 = __builtin_amdgcn_cvt_f32_fp8(cur.sc[t], 1);
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
                             float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
-                            for (int p = 0; p < 8; ++p) p0 = dot2_bf16(xv[p], wb[t][p], p0);
+                            for (int p = 0; p < 8; ++p) p0 = dot2_bf16(xv[r][p], wb[p], p0);
 #pragma unroll
-                            for (int p = 8; p < 16; ++p) p1 = dot2_bf16(xv[p], wb[t][p], p1);
+                            for (int p = 8; p < 16; ++p) p1 = dot2_bf16(xv[r][p], wb[p], p1);
                             float a = acc[r * T + t];
-                            a = __builtin_fmaf(bsf[t][0], p0, a);
-                            a = __builtin_fmaf(bsf[t][1], p1, a);
+                            a = __builtin_fmaf(b0, p0, a);
+                            a = __builtin_fmaf(b1, p1, a);
                             acc[r * T + t] = a;
                         }
                     }
-                }
-                wave_reduce_scatter<NP>(acc, lane);
+                } else {
+                uint32_t wb[T][16];
+                float bsf[T][2];
 #pragma unroll
-                for (int j = 0; j < MAXB; ++j)
-                    if (j == bi) part[j] = (tt == 0) ? acc[0] : part[j] + acc[0];
+                for (int t = 0; t < T; ++t) {
+                    const uint32_t d[4] = {cur.w[t].x, cur.w[t].y, cur.w[t].z, cur.w[t].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        wb[t][4 * i + 0] = e2m1x2_to_bf16<0>(d[i]);
+                        wb[t][4 * i + 1] = e2m1x2_to_bf16<1>(d[i]);
+                        wb[t][4 * i + 2] = e2m1x2_to_bf16<2>(d[i]);
+                        wb[t][4 * i + 3] = e2m1x2_to_bf16<3>(d[i]);
+                    }
+                    bsf[t][0] = __builtin_amdgcn_cvt_f32_fp8(cur.sc[t], 0);
+                    bsf[t][1] = __builtin_amdgcn_cvt_f32_fp8(cur.sc[t], 1);
+                }
+                // Activation rows through a two-entry ring: row r + 1 is read
+                // while row r is computed.
+                uint4 xr[2][4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) xr[0][c] = xrow[64 * c];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if (r + 1 < R) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            xr[(r + 1) & 1][c] = xrow[(r + 1) * kF4VecPerTileRow + 64 * c];
+                    }
+                    uint32_t xv[16];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        xv[4 * c + 0] = xr[r & 1][c].x;
+                        xv[4 * c + 1] = xr[r & 1][c].y;
+                        xv[4 * c + 2] = xr[r & 1][c].z;
+                        xv[4 * c + 3] = xr[r & 1][c].w;
+                    }
+#pragma unroll
+                    for (int t = 0; t < T; ++t) {
+                        float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+                        for (int p = 0; p < 8; ++p) p0 = dot2_bf16(xv[p], wb[t][p], p0);
+#pragma unroll
+                        for (int p = 8; p < 16; ++p) p1 = dot2_bf16(xv[p], wb[t][p], p1);
+                        float a = acc[r * T + t];
+                        a = __builtin_fmaf(bsf[t][0], p0, a);
+                        a = __builtin_fmaf(bsf[t][1], p1, a);
+                        acc[r * T + t] = a;
+                    }
+                }
+                }
+                if (s + 1 == nseg) {
+                    wave_reduce_scatter<NP>(acc, lane);
+#pragma unroll
+                    for (int j = 0; j < MAXB; ++j)
+                        if (j == bi) part[j] = (tt == 0) ? acc[0] : part[j] + acc[0];
+                    ++bi;
+                    s = 0;
+                } else {
+                    ++s;
+                }
+            };
+            Item bufA, bufB;
+            if (nitems > 0) load_item(0, 0, bufA);
+            int it = 0;
+#pragma unroll 1
+            for (; it + 1 < nitems; it += 2) {
+                step(it, bufA, bufB);
+                step(it + 1, bufB, bufA);
             }
+            if (it < nitems) step(it, bufA, bufB);
         }
 
 #pragma unroll
         for (int bi = 0; bi < MAXB; ++bi) {
             const int band = (sj * MAXB + bi) * TW + gw;
-            if (band >= NB) break;
             const int v = band * T + my_t;
-            if (writer && v < V) out[(size_t)my_r * V + v] = f32_to_bf16_rne(g * part[bi]);
+            if (writer && band < NB && v < V)
+                out[(size_t)my_r * V + v] = f32_to_bf16_rne(g * part[bi]);
         }
     }
 }
 
-template <int R, int T, int WAVES, int MAXB>
+template <int R, int T, int WAVES, int MAXB, int BPC>
 static hipError_t launch_nvfp4(const uint8_t* Wp, const uint8_t* bs, const uint16_t* x, float g,
                                int H, int V, uint16_t* out, const DeviceInfo& dev,
                                hipStream_t stream) {
     const int64_t NB = (V + T - 1) / T;
     int64_t blocks = (NB + WAVES - 1) / WAVES;
-    if (blocks > dev.num_cus) blocks = dev.num_cus;
+    if (blocks > (int64_t)dev.num_cus * BPC) blocks = (int64_t)dev.num_cus * BPC;
     const int64_t TW = blocks * WAVES;
     const int64_t per_wave = (NB + TW - 1) / TW;
     const int nsuper = (int)((per_wave + MAXB - 1) / MAXB);
-    hipLaunchKernelGGL((nvfp4_gemv_kernel<R, T, WAVES, MAXB>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((nvfp4_gemv_kernel<R, T, WAVES, MAXB, BPC>), dim3((unsigned)blocks),
                        dim3(WAVES * kWave), 0, stream, Wp, bs, x, g, H, V, out, nsuper);
     return hipGetLastError();
 }
@@ -189,17 +265,17 @@ static hipError_t launch_nvfp4(const uint8_t* Wp, const uint8_t* bs, const uint1
 hipError_t run_nvfp4(const uint8_t* Wp, const uint8_t* bs, const uint16_t* x, float g, int R,
                      int H, int V, uint16_t* out, const DeviceInfo& dev, hipStream_t stream) {
     switch (R) {
-#define QH_F4_CASE(RR, TT, MB) \
-    case RR:                   \
-        return launch_nvfp4<RR, TT, 16, MB>(Wp, bs, x, g, H, V, out, dev, stream);
-        QH_F4_CASE(1, 4, 12)
-        QH_F4_CASE(2, 4, 12)
-        QH_F4_CASE(3, 4, 12)
-        QH_F4_CASE(4, 4, 12)
-        QH_F4_CASE(5, 2, 20)
-        QH_F4_CASE(6, 2, 20)
-        QH_F4_CASE(7, 2, 20)
-        QH_F4_CASE(8, 2, 20)
+#define QH_F4_CASE(RR, TT, WV, MB, BPC) \
+    case RR:                            \
+        return launch_nvfp4<RR, TT, WV, MB, BPC>(Wp, bs, x, g, H, V, out, dev, stream);
+        QH_F4_CASE(1, 2, 16, 20, 1)
+        QH_F4_CASE(2, 2, 16, 20, 1)
+        QH_F4_CASE(3, 2, 16, 20, 1)
+        QH_F4_CASE(4, 2, 16, 20, 1)
+        QH_F4_CASE(5, 4, 8, 12, 1)
+        QH_F4_CASE(6, 4, 8, 12, 1)
+        QH_F4_CASE(7, 4, 8, 12, 1)
+        QH_F4_CASE(8, 4, 8, 12, 1)
 #undef QH_F4_CASE
         default:
             return hipErrorInvalidValue;

@@ -22,23 +22,29 @@
 // aligned dwords and realigned with v_alignbyte (the extra dword stays
 // inside the super-block). The -32 offset is folded into the integer dot:
 // the staging step stores -32 * sum(q8) per sub-block next to the q8 values.
+// Weight loads are ordinary (cached) loads, not streaming ones: the ql, qh,
+// scale and d fields of one super-block share 128-byte lines across several
+// load instructions, and streaming loads re-fetched those lines (about 8 %
+// more HBM bytes and 25 % more time, measured).
 #include "qhead_device.h"
 #include "qhead_internal.h"
 
 namespace qh {
 
-constexpr int kQSegK = 1024;                 // 4 super-blocks per wave segment
 constexpr int kQTileK = 8192;                // k per LDS tile (32 super-blocks)
 constexpr int kQSbPerTile = kQTileK / 256;
 
+// LDS per workgroup, sized by the row count so that small R leaves room for
+// several workgroups per CU.
+template <int R>
 struct Q6Lds {
-    int8_t q[8][kQTileK];               // q8 values [row][k]
-    float d8[8][kQTileK / 32];          // fp16 d of each q8 block, as f32
-    int32_t off[8][kQTileK / 16];       // -32 * sum of q8 over each 16-value sub-block
+    int8_t q[R][kQTileK];               // q8 values [row][k]
+    float d8[R][kQTileK / 32];          // fp16 d of each q8 block, as f32
+    int32_t off[R][kQTileK / 16];       // -32 * sum of q8 over each 16-value sub-block
 };
 
 template <int R, int NTHREADS>
-__device__ __forceinline__ void q6_stage_tile(Q6Lds& L, const uint8_t* q8, int H, int k0,
+__device__ __forceinline__ void q6_stage_tile(Q6Lds<R>& L, const uint8_t* q8, int H, int k0,
                                               int klen) {
     const int nb = H / 32;
     const int jb0 = k0 / 32;
@@ -65,31 +71,18 @@ __device__ __forceinline__ void q6_stage_tile(Q6Lds& L, const uint8_t* q8, int H
     }
 }
 
-// Sixteen bytes at a 2-byte-aligned address inside a super-block, read as
-// five aligned dwords (the fifth never leaves the super-block) and realigned.
-__device__ __forceinline__ void load16_a2(const uint8_t* p, uint32_t (&o)[4]) {
-    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-    const uint32_t* q = reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3);
-    const uint32_t sh = (uint32_t)(a & 3);
-    uint32_t d[5];
-#pragma unroll
-    for (int i = 0; i < 5; ++i) d[i] = __builtin_nontemporal_load(q + i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = __builtin_amdgcn_alignbyte(d[i + 1], d[i], sh);
-}
-
-template <int R, int T, int WAVES, int MAXB>
-__global__ void __launch_bounds__(WAVES * kWave)
+template <int R, int T, int WAVES, int MAXB, int BPC>
+__global__ void __launch_bounds__(WAVES * kWave, (WAVES * BPC + 3) / 4)
 q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ q8, int H, int V,
                 uint16_t* __restrict__ out, int nsuper) {
     constexpr int N = T * R;
     constexpr int NP = next_pow2(N);
     constexpr int M = Log2<NP>::value;
     static_assert(NP <= 64 && R <= 8, "T*R must be <= 64, R <= 8");
-    __shared__ Q6Lds L;
+    __shared__ Q6Lds<R> L;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int TW = gridDim.x * WAVES;
     const int gw = blockIdx.x * WAVES + wave;
     const int NB = (V + T - 1) / T;
@@ -111,6 +104,18 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     const int my_t = my_idx - my_r * T;
     const bool writer = ((lane & ((1 << (6 - M)) - 1)) == 0) && (my_idx < N);
 
+    // Raw bytes of one item: for each of T rows, the lane's 16 ql and 16 qh
+    // bytes as five aligned dwords each (a 210-byte super-block is only
+    // 2-byte aligned; the fifth dword stays inside the super-block), its
+    // int8 scale and the fp16 d.
+    struct Item {
+        uint32_t ql[T][5];
+        uint32_t qh[T][5];
+        uint32_t sc[T];
+        uint32_t d[T];
+        uint32_t sh[T];
+    };
+
     for (int sj = 0; sj < nsuper; ++sj) {
         float part[MAXB];
 #pragma unroll
@@ -126,92 +131,119 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                 q6_stage_tile<R, WAVES * kWave>(L, q8, H, k0, klen);
                 __syncthreads();
             }
-#pragma unroll 1
-            for (int bi = 0; bi < MAXB; ++bi) {
-                const int band = (sj * MAXB + bi) * TW + gw;
-                if (band >= NB) break;
-                const int v0 = band * T;
-                float acc[NP];
+            const int first = (sj * MAXB) * TW + gw;
+            const int nbb = first < NB ? min(MAXB, (NB - 1 - first) / TW + 1) : 0;
+            const int nitems = nbb * nseg;
+            // Unconditional loads: lanes past the last super-block of the
+            // row re-read the last one and rows past the vocab tail re-read
+            // the last row; their contributions are zeroed or never stored.
+            auto load_item = [&](int bi, int s, Item& dst) {
+                const int v0 = ((sj * MAXB + bi) * TW + gw) * T;
+                const int sb = min(tt * kQSbPerTile + s * 4 + sbi, nsb - 1);
 #pragma unroll
-                for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
-
-                for (int s = 0; s < nseg; ++s) {
-                    const int sbt = s * 4 + sbi;          // super-block within the tile
-                    const bool sin = sbt < nsb_tile;
-                    const int sb = tt * kQSbPerTile + sbt;  // super-block within the row
-                    uint32_t qw[T][4];
-                    float dsc[T];
-                    int scv[T];
+                for (int t = 0; t < T; ++t) {
+                    const int v = min(v0 + t, V - 1);
+                    const uint8_t* blk = blocks + (size_t)v * rowbytes + (size_t)sb * kQ6KBlockBytes;
+                    const uintptr_t a = reinterpret_cast<uintptr_t>(blk);
+                    const uint32_t* base = reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3);
+                    dst.sh[t] = (uint32_t)(a & 3);
+#pragma unroll
+                    for (int i = 0; i < 5; ++i) {
+                        dst.ql[t][i] = base[ql_off / 4 + i];
+                        dst.qh[t][i] = base[qh_off / 4 + i];
+                    }
+                    dst.sc[t] = blk[192 + t16];
+                    dst.d[t] = *reinterpret_cast<const uint16_t*>(blk + 208);
+                }
+            };
+            float acc[NP];
+            int bi = 0, s = 0;
+            auto step = [&](int it, const Item& cur, Item& nxt) {
+                {
+                    const bool last = it + 1 >= nitems;
+                    const int nbi = last ? bi : ((s + 1 == nseg) ? bi + 1 : bi);
+                    const int ns = last ? s : ((s + 1 == nseg) ? 0 : s + 1);
+                    load_item(nbi, ns, nxt);
+                }
+                if (s == 0) {
+#pragma unroll
+                    for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
+                }
+                const int sbt = s * 4 + sbi;  // super-block within the tile
+                const bool valid = sbt < nsb_tile;
+                uint32_t qw[T][4];
+                float wsc[T];
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t ql =
+                            __builtin_amdgcn_alignbyte(cur.ql[t][i + 1], cur.ql[t][i], cur.sh[t]);
+                        const uint32_t qh =
+                            __builtin_amdgcn_alignbyte(cur.qh[t][i + 1], cur.qh[t][i], cur.sh[t]);
+                        qw[t][i] = ((ql >> lo_shift) & 0x0F0F0F0Fu) |
+                                   (((qh >> hi_shift) & 0x03030303u) << 4);
+                    }
+                    // d * sc is exact in FP32 (11-bit times 8-bit significands)
+                    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)cur.d[t]);
+                    wsc[t] = valid ? d * (float)(int)(int8_t)cur.sc[t] : 0.0f;
+                }
+                const int kk = min(sbt, kQSbPerTile - 1) * 256 + 16 * t16;  // k within the tile
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const uint4 xq = *reinterpret_cast<const uint4*>(&L.q[r][kk]);
+                    const int off = L.off[r][kk >> 4];
+                    const float d8 = valid ? L.d8[r][kk >> 5] : 0.0f;
 #pragma unroll
                     for (int t = 0; t < T; ++t) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) qw[t][i] = 0;
-                        dsc[t] = 0.0f;
-                        scv[t] = 0;
-                        if (v0 + t < V && sin) {
-                            const uint8_t* blk = blocks + (size_t)(v0 + t) * rowbytes +
-                                                 (size_t)sb * kQ6KBlockBytes;
-                            uint32_t ql[4], qh[4];
-                            load16_a2(blk + ql_off, ql);
-                            load16_a2(blk + qh_off, qh);
-                            const uint16_t dbits = *reinterpret_cast<const uint16_t*>(blk + 208);
-                            dsc[t] = (float)__builtin_bit_cast(_Float16, dbits);
-                            scv[t] = (int)(int8_t)blk[192 + t16];
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const uint32_t lo = (ql[i] >> lo_shift) & 0x0F0F0F0Fu;
-                                const uint32_t hi = ((qh[i] >> hi_shift) & 0x03030303u) << 4;
-                                qw[t][i] = lo | hi;
-                            }
-                        }
-                    }
-                    if (sin) {
-                        const int kk = sbt * 256 + 16 * t16;   // k within the tile
-                        const int jt = kk >> 5;                 // q8 block within the tile
-#pragma unroll
-                        for (int r = 0; r < R; ++r) {
-                            const uint4 xq = *reinterpret_cast<const uint4*>(&L.q[r][kk]);
-                            const int off = L.off[r][kk >> 4];
-                            const float d8 = L.d8[r][jt];
-#pragma unroll
-                            for (int t = 0; t < T; ++t) {
-                                int is = __builtin_amdgcn_sdot4((int)qw[t][0], (int)xq.x, off, false);
-                                is = __builtin_amdgcn_sdot4((int)qw[t][1], (int)xq.y, is, false);
-                                is = __builtin_amdgcn_sdot4((int)qw[t][2], (int)xq.z, is, false);
-                                is = __builtin_amdgcn_sdot4((int)qw[t][3], (int)xq.w, is, false);
-                                const float f = (float)(is * scv[t]);
-                                acc[r * T + t] = __builtin_fmaf(f, dsc[t] * d8, acc[r * T + t]);
-                            }
-                        }
+                        int is = __builtin_amdgcn_sdot4((int)qw[t][0], (int)xq.x, off, false);
+                        is = __builtin_amdgcn_sdot4((int)qw[t][1], (int)xq.y, is, false);
+                        is = __builtin_amdgcn_sdot4((int)qw[t][2], (int)xq.z, is, false);
+                        is = __builtin_amdgcn_sdot4((int)qw[t][3], (int)xq.w, is, false);
+                        acc[r * T + t] = __builtin_fmaf((float)is, wsc[t] * d8, acc[r * T + t]);
                     }
                 }
-                wave_reduce_scatter<NP>(acc, lane);
+                if (s + 1 == nseg) {
+                    wave_reduce_scatter<NP>(acc, lane);
 #pragma unroll
-                for (int j = 0; j < MAXB; ++j)
-                    if (j == bi) part[j] = (tt == 0) ? acc[0] : part[j] + acc[0];
+                    for (int j = 0; j < MAXB; ++j)
+                        if (j == bi) part[j] = (tt == 0) ? acc[0] : part[j] + acc[0];
+                    ++bi;
+                    s = 0;
+                } else {
+                    ++s;
+                }
+            };
+            Item bufA, bufB;
+            if (nitems > 0) load_item(0, 0, bufA);
+            int it = 0;
+#pragma unroll 1
+            for (; it + 1 < nitems; it += 2) {
+                step(it, bufA, bufB);
+                step(it + 1, bufB, bufA);
             }
+            if (it < nitems) step(it, bufA, bufB);
         }
 
 #pragma unroll
         for (int bi = 0; bi < MAXB; ++bi) {
             const int band = (sj * MAXB + bi) * TW + gw;
-            if (band >= NB) break;
             const int v = band * T + my_t;
-            if (writer && v < V) out[(size_t)my_r * V + v] = f32_to_bf16_rne(part[bi]);
+            if (writer && band < NB && v < V) out[(size_t)my_r * V + v] = f32_to_bf16_rne(part[bi]);
         }
     }
 }
 
-template <int R, int T, int WAVES, int MAXB>
+template <int R, int T, int WAVES, int MAXB, int BPC>
 static hipError_t launch_q6k(const uint8_t* blocks, const uint8_t* q8, int H, int V,
                              uint16_t* out, const DeviceInfo& dev, hipStream_t stream) {
     const int64_t NB = (V + T - 1) / T;
     int64_t nblk = (NB + WAVES - 1) / WAVES;
-    if (nblk > dev.num_cus) nblk = dev.num_cus;
+    if (nblk > (int64_t)dev.num_cus * BPC) nblk = (int64_t)dev.num_cus * BPC;
     const int64_t TW = nblk * WAVES;
     const int64_t per_wave = (NB + TW - 1) / TW;
     const int nsuper = (int)((per_wave + MAXB - 1) / MAXB);
-    hipLaunchKernelGGL((q6k_gemv_kernel<R, T, WAVES, MAXB>), dim3((unsigned)nblk),
+    hipLaunchKernelGGL((q6k_gemv_kernel<R, T, WAVES, MAXB, BPC>), dim3((unsigned)nblk),
                        dim3(WAVES * kWave), 0, stream, blocks, q8, H, V, out, nsuper);
     return hipGetLastError();
 }
@@ -219,17 +251,17 @@ static hipError_t launch_q6k(const uint8_t* blocks, const uint8_t* q8, int H, in
 hipError_t run_q6k(const uint8_t* blocks, const uint8_t* q8, int R, int H, int V, uint16_t* out,
                    const DeviceInfo& dev, hipStream_t stream) {
     switch (R) {
-#define QH_Q6_CASE(RR, TT, MB) \
-    case RR:                   \
-        return launch_q6k<RR, TT, 16, MB>(blocks, q8, H, V, out, dev, stream);
-        QH_Q6_CASE(1, 4, 12)
-        QH_Q6_CASE(2, 4, 12)
-        QH_Q6_CASE(3, 4, 12)
-        QH_Q6_CASE(4, 4, 12)
-        QH_Q6_CASE(5, 2, 20)
-        QH_Q6_CASE(6, 2, 20)
-        QH_Q6_CASE(7, 2, 20)
-        QH_Q6_CASE(8, 2, 20)
+#define QH_Q6_CASE(RR, TT, WV, MB, BPC) \
+    case RR:                            \
+        return launch_q6k<RR, TT, WV, MB, BPC>(blocks, q8, H, V, out, dev, stream);
+        QH_Q6_CASE(1, 2, 16, 20, 1)
+        QH_Q6_CASE(2, 2, 16, 20, 1)
+        QH_Q6_CASE(3, 2, 16, 20, 1)
+        QH_Q6_CASE(4, 2, 16, 20, 1)
+        QH_Q6_CASE(5, 4, 8, 12, 1)
+        QH_Q6_CASE(6, 4, 8, 12, 1)
+        QH_Q6_CASE(7, 4, 8, 12, 1)
+        QH_Q6_CASE(8, 4, 8, 12, 1)
 #undef QH_Q6_CASE
         default:
             return hipErrorInvalidValue;
