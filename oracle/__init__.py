@@ -89,6 +89,9 @@ def lib():
             "orc_prep_nvfp4_global": (ctypes.c_float, [ctypes.c_float]),
             "orc_prep_nvfp4_rows": (None, [f32p, i64, i32, ctypes.c_float, u8p, u8p]),
             "orc_prep_q6k_rows": (None, [f32p, i64, i32, u8p]),
+            "orc_dequant_nvfp4_bf16": (None, [u8p, u8p, ctypes.c_float, i64, i32, u16p]),
+            "orc_e8m0": (ctypes.c_double, [ctypes.c_uint8]),
+            "orc_dequant_fp4_e8m0_bf16": (None, [u8p, u8p, i64, i64, u16p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -342,3 +345,32 @@ def prep_config_weights(cfg_index: int, fmt: str, *, vocab=None, hidden=None, st
             blocks[lo:hi] = prep_q6k_rows(wf)
         return blocks
     raise ValueError(fmt)
+
+
+# ------------------------------------------------------ load-time dequant
+
+def e8m0_value(code: int) -> float:
+    return float(lib().orc_e8m0(int(code) & 0xFF))
+
+
+def dequant_nvfp4_bf16(wp: np.ndarray, bs: np.ndarray, g: float) -> np.ndarray:
+    """NVFP4 [n][k] -> BF16 bits [n][k]: bf16(fl32((e2m1 * e4m3(bs)) * g))."""
+    wp = np.ascontiguousarray(wp, dtype=np.uint8)
+    bs = np.ascontiguousarray(bs, dtype=np.uint8)
+    n, k = wp.shape[0], wp.shape[1] * 2
+    assert bs.shape == (n, k // 16)
+    out = np.empty((n, k), dtype=np.uint16)
+    lib().orc_dequant_nvfp4_bf16(_ptr(wp, ctypes.c_uint8), _ptr(bs, ctypes.c_uint8), float(g), n, k,
+                                 _ptr(out, ctypes.c_uint16))
+    return out
+
+
+def dequant_fp4_e8m0_bf16(packed: np.ndarray, scales: np.ndarray, total: int) -> np.ndarray:
+    """Flat E2M1 with E8M0 group scales -> BF16 bits [total]."""
+    p = np.ascontiguousarray(packed, dtype=np.uint8).ravel()
+    s = np.ascontiguousarray(scales, dtype=np.uint8).ravel()
+    assert p.size * 2 == total and total % s.size == 0
+    out = np.empty(total, dtype=np.uint16)
+    lib().orc_dequant_fp4_e8m0_bf16(_ptr(p, ctypes.c_uint8), _ptr(s, ctypes.c_uint8), total, s.size,
+                                    _ptr(out, ctypes.c_uint16))
+    return out

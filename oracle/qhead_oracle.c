@@ -165,6 +165,7 @@ ORC_API uint16_t orc_bf16_rne(double v) {
     uint16_t sign = signbit(v) ? 0x8000 : 0;
     double a = fabs(v);
     if (a == 0.0) return sign;
+    if (isinf(a)) return 0x7F80 | sign;
     int ex;
     frexp(a, &ex);
     int e = ex - 1;
@@ -526,6 +527,57 @@ ORC_API void orc_prep_q6k_rows(const float* wf, int64_t nrows, int hidden, uint8
                     blk[128 + 32 * n2 + l] |= (uint8_t)(((q >> 4) & 3) << (2 * c));
                 }
             }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Load-time dequantization to BF16                                    */
+/* ------------------------------------------------------------------ */
+
+/* NVFP4 -> BF16 for a [n][k] weight ("fp8_lut.rs", dequant_nvfp4_to_bf16:
+ * value E2M1 * fp8 block scale * global multiplier, even flat index = low
+ * nibble). Reading of the rounding: the E2M1 x E4M3 product is exact in
+ * binary32, the global multiplier is applied in binary32 (one rounding) and
+ * the result is rounded to BF16, nearest even:
+ *   out = bf16( fl32( (e2m1 * e4m3(bs)) * g ) ). */
+ORC_API void orc_dequant_nvfp4_bf16(const uint8_t* packed, const uint8_t* bs, float g, int64_t n,
+                                    int k, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t v = 0; v < n; v++) {
+        for (int c = 0; c < k; c++) {
+            int64_t flat = v * (int64_t)k + c;
+            uint8_t byte = packed[flat / 2];
+            uint8_t nib = (flat % 2 == 0) ? (byte & 15) : (byte >> 4);
+            float w = (float)(orc_e2m1(nib) * orc_e4m3(bs[v * (int64_t)(k / 16) + c / 16]));
+            float y = w * g;
+            out[flat] = orc_bf16_rne((double)y);
+        }
+    }
+}
+
+/* E8M0 scale byte -> value: 2^(e - 127) for e = 1..254; e = 0 and e = 255
+ * (NaN) give 0 ("fp8_lut.rs", FP8_E8M0_LUT and fp8_e8m0_to_f32). */
+ORC_API double orc_e8m0(uint8_t e) {
+    if (e == 0 || e == 255) return 0.0;
+    return ldexp(1.0, (int)e - 127);
+}
+
+/* E2M1 with E8M0 per-group scales and no global -> BF16, over a flat tensor
+ * of `total` values in `groups` groups of total/groups consecutive values
+ * ("fp8_lut.rs", dequant_nvfp4_e8m0_to_bf16): out = bf16(fl32(e2m1 * scale)). */
+ORC_API void orc_dequant_fp4_e8m0_bf16(const uint8_t* packed, const uint8_t* scales,
+                                       int64_t total, int64_t groups, uint16_t* out) {
+    int64_t block = total / groups;
+#pragma omp parallel for schedule(static)
+    for (int64_t gi = 0; gi < groups; gi++) {
+        double sc = orc_e8m0(scales[gi]);
+        for (int64_t e = 0; e < block; e++) {
+            int64_t flat = gi * block + e;
+            uint8_t byte = packed[flat / 2];
+            uint8_t nib = (flat % 2 == 0) ? (byte & 15) : (byte >> 4);
+            float y = (float)(orc_e2m1(nib) * sc); /* exact unless it leaves binary32's range */
+            out[flat] = orc_bf16_rne((double)y);
         }
     }
 }

@@ -457,3 +457,147 @@ def test_synth_row_ranges_are_stable():
     assert np.array_equal(x4, x40[:4])
     cols = synth.outlier_columns(1, 4096, 41)
     assert len(cols) == 41
+
+
+# ------------------------------------------------ load-time FP4 -> BF16
+
+def _g_value(tok):
+    if tok.startswith("0x"):
+        return float(_bits_f32(int(tok, 16)))
+    return float(tok)
+
+
+def test_e8m0_table_as_printed():
+    for code, val in _rows("e8m0_table.txt"):
+        assert oracle.e8m0_value(int(code)) == float(val), code
+
+
+def test_e8m0_matches_exponent_field_construction():
+    # 2^(e-127) is the binary32 whose exponent field is e and mantissa 0
+    for e in range(1, 255):
+        assert oracle.e8m0_value(e) == float(_bits_f32(e << 23)), e
+    assert oracle.e8m0_value(0) == 0.0 and oracle.e8m0_value(255) == 0.0
+
+
+def test_dequant_hand_values():
+    for kind, byte, sc, g, even, odd in _rows("dequant_hand.txt"):
+        b, s = int(byte, 16), int(sc, 0)
+        if kind == "nvfp4":
+            wp = np.zeros((1, 16), dtype=np.uint8)
+            wp[0, 0] = b
+            bs = np.array([[s, s]], dtype=np.uint8)
+            out = oracle.dequant_nvfp4_bf16(wp, bs, _g_value(g))[0]
+        else:
+            packed = np.zeros(8, dtype=np.uint8)
+            packed[0] = b
+            out = oracle.dequant_fp4_e8m0_bf16(packed, np.array([s], dtype=np.uint8), 16)
+        assert int(out[0]) == int(even, 16), (kind, byte, sc, g)
+        assert int(out[1]) == int(odd, 16), (kind, byte, sc, g)
+        assert not out[2:].any()
+
+
+def _torch_e2m1_all():
+    vals = [float(v) for _, v in _rows("e2m1_table.txt")]
+    return torch.tensor(vals, dtype=torch.float32)
+
+
+def _nibbles(packed: np.ndarray) -> np.ndarray:
+    p = packed.reshape(-1)
+    out = np.empty(p.size * 2, dtype=np.int64)
+    out[0::2] = p & 15
+    out[1::2] = p >> 4
+    return out
+
+
+def test_dequant_nvfp4_matches_torch_casts():
+    # the same value built from library casts: E2M1 table values times the
+    # torch float8_e4m3fn decode of the block scale, binary32 products, and
+    # torch's BF16 cast (nearest even)
+    rng = np.random.default_rng(11)
+    n, k = 7, 96
+    wp = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    bs = rng.integers(0, 256, size=(n, k // 16), dtype=np.uint8)
+    bs[bs == 0x7F] = 0x41
+    bs[bs == 0xFF] = 0xC1
+    for g in (1.0, float(np.float32(0.37)), float(np.float32(3.1e-3)), 0.0):
+        got = oracle.dequant_nvfp4_bf16(wp, bs, g)
+        e2 = _torch_e2m1_all()[torch.from_numpy(_nibbles(wp))].reshape(n, k)
+        s = torch.from_numpy(bs).view(torch.float8_e4m3fn).to(torch.float32)
+        s = s.repeat_interleave(16, dim=1)
+        y = (e2 * s) * torch.tensor(g, dtype=torch.float32)
+        ref = y.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, ref), g
+
+
+def test_dequant_e8m0_matches_torch_casts():
+    rng = np.random.default_rng(12)
+    groups, block = 256, 32
+    total = groups * block
+    packed = rng.integers(0, 256, size=total // 2, dtype=np.uint8)
+    scales = np.arange(256, dtype=np.uint8)  # every code once
+    got = oracle.dequant_fp4_e8m0_bf16(packed, scales, total)
+    sc = torch.from_numpy((scales.astype(np.uint32) << 23).view(np.float32).copy())
+    sc[0] = 0.0
+    sc[255] = 0.0
+    e2 = _torch_e2m1_all()[torch.from_numpy(_nibbles(packed))]
+    y = e2 * sc.repeat_interleave(block)
+    ref = y.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_dequant_e8m0_group_boundaries():
+    # groups of 48 values: the scale changes exactly at flat index 48 and 96
+    packed = np.full(72, 0x22, dtype=np.uint8)  # every nibble = 1.0
+    out = oracle.dequant_fp4_e8m0_bf16(packed, np.array([127, 128, 126], dtype=np.uint8), 144)
+    assert (out[:48] == 0x3F80).all() and (out[48:96] == 0x4000).all()
+    assert (out[96:] == 0x3F00).all()
+
+
+# ------------------------------------------- NVFP4 / Q6_K weight preparation
+
+def test_prep_nvfp4_rows_nearest_codes():
+    wf = synth.weight_rows_f32(4, 0, 24, hidden=512)
+    wf[5] = 0
+    g = oracle.nvfp4_global(float(np.abs(wf).max()))
+    assert g == np.float32(np.abs(wf).max()) / np.float32(2688)
+    packed, bs = oracle.prep_nvfp4_rows(wf, g)
+    assert not packed[5].any() and not bs[5].any()
+    T = _torch_e4m3_decode_all()
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float64)
+    nib = _nibbles(packed).reshape(wf.shape)
+    for v in (0, 1, 23):
+        amax = np.abs(wf[v].reshape(-1, 16)).max(axis=1)
+        code = _torch_e4m3_encode(amax / (np.float32(6) * np.float32(g)))
+        assert np.array_equal(bs[v], code)
+        step = (T[bs[v]].astype(np.float32) * np.float32(g)).repeat(16)
+        t = np.abs((wf[v] / step).astype(np.float64))
+        # brute force: the code's magnitude is a nearest E2M1 magnitude
+        dist = np.abs(t[:, None] - mags[None, :])
+        best = dist.min(axis=1)
+        mine = dist[np.arange(t.size), nib[v] & 7]
+        assert np.array_equal(mine, best)
+        nz = (nib[v] & 7) != 0
+        assert np.array_equal((nib[v][nz] >> 3) == 1, wf[v][nz] < 0)
+
+
+def test_prep_q6k_rows_nearest_levels():
+    wf = synth.weight_rows_f32(4, 0, 6, hidden=512)
+    wf[2, :256] = 0
+    blocks = oracle.prep_q6k_rows(wf)
+    sb = blocks.reshape(6, 2, 210)
+    zero = oracle.q6k_decode_block(sb[2, 0])
+    assert not zero.any() and sb[2, 0, 208:].view(np.uint16)[0] == 0
+    for v in (0, 3, 5):
+        for b in range(2):
+            w = wf[v, 256 * b:256 * (b + 1)]
+            st = np.abs(w.reshape(16, 16)).max(axis=1) / np.float32(31)
+            d16 = np.float16(st.max() / np.float32(127))
+            assert sb[v, b, 208:].view(np.float16)[0] == d16
+            d = np.float32(d16)
+            sc = np.clip(np.rint(st / d), 0, 127).astype(np.int64)
+            assert np.array_equal(sb[v, b, 192:208].astype(np.int64), sc)
+            step = (d * sc.astype(np.float32)).repeat(16)
+            dec = oracle.q6k_decode_block(sb[v, b])
+            # decoded weights are the clamped nearest levels of the step grid
+            q = np.clip(np.rint(w / step), -32, 31)
+            assert np.array_equal(dec, q * step.astype(np.float64))
