@@ -197,6 +197,47 @@ int qhead_q6k(const uint8_t* blocks, const void* scales, const uint16_t* x_bf16,
 int qhead_quantize_fp8_rows(const float* w_f32, int32_t vocab, int32_t hidden, uint8_t* w_e4m3,
                             float* row_scale, void* stream);
 
+/* Weight preparation, NVFP4 with global multiplier g (no page prints a
+ * quantizer; value formula of "fp8_lut.rs" dequant_nvfp4_to_bf16): per block
+ * of 16 values of a row, scale = e4m3_rne_sat(fl32(amax / fl32(6 g))),
+ * step = fl32(e4m3(scale) * g), nibble = e2m1_rne_sat(fl32(w / step)) (ties
+ * to the even code, sign kept; 0 where step is 0); even k in the low nibble.
+ *  w_f32 [vocab][hidden], 16-byte aligned; w_packed [vocab][hidden/2],
+ *  8-byte aligned; block_scale [vocab][hidden/16]. hidden % 16 == 0. */
+int qhead_quantize_nvfp4_rows(const float* w_f32, int32_t vocab, int32_t hidden,
+                              float global_scale, uint8_t* w_packed, uint8_t* block_scale,
+                              void* stream);
+
+/* Weight preparation, Q6_K super-blocks (layout of qhead_q6k_gemv): per 16
+ * values s_t = fl32(amax_t / 31); d = fp16(fl32(max_t s_t / 127));
+ * sc_t = clamp(rne(fl32(s_t / d)), 0, 127); q = clamp(rne(fl32(w /
+ * fl32(d * sc_t))), -32, 31) + 32 (32 where the step is 0).
+ *  w_f32 [vocab][hidden], 16-byte aligned; blocks [vocab][hidden/256][210],
+ *  2-byte aligned. hidden % 256 == 0. */
+int qhead_quantize_q6k_rows(const float* w_f32, int32_t vocab, int32_t hidden, uint8_t* blocks,
+                            void* stream);
+
+/* Load-time NVFP4 -> BF16 of a [rows][cols] weight ("fp8_lut.rs",
+ * dequant_nvfp4_to_bf16: value E2M1 * E4M3 block scale * global multiplier,
+ * even flat index = low nibble):
+ *   out = bf16_rne( fl32( (e2m1 * e4m3(scale)) * global_scale ) ).
+ *  w_packed [rows][cols/2], 16-byte aligned; block_scale [rows][cols/16],
+ *  2-byte aligned; out_bf16 [rows][cols], 16-byte aligned; cols % 32 == 0.
+ *  A caller holding the reciprocal global passes 1/g (0 when g == 0). */
+int qhead_dequant_nvfp4_bf16(const uint8_t* w_packed, const uint8_t* block_scale, int32_t rows,
+                             int32_t cols, float global_scale, uint16_t* out_bf16, void* stream);
+
+/* Load-time E2M1 with E8M0 group scales and no global -> BF16 over a flat
+ * tensor of `total` values in `num_groups` groups of total/num_groups
+ * consecutive values ("fp8_lut.rs", dequant_nvfp4_e8m0_to_bf16 and the
+ * FP8_E8M0_LUT: scale 2^(e-127) for e = 1..254, 0 for e = 0 and e = 255):
+ *   out = bf16_rne( fl32(e2m1 * scale) ).
+ *  QHEAD_ERR_SHAPE unless total % num_groups == 0 (as the page requires) and
+ *  the group size is a multiple of 16. w_packed [total/2] bytes, 8-byte
+ *  aligned; scale_e8m0 [num_groups]; out_bf16 [total], 16-byte aligned. */
+int qhead_dequant_fp4_e8m0_bf16(const uint8_t* w_packed, const uint8_t* scale_e8m0, int64_t total,
+                                int64_t num_groups, uint16_t* out_bf16, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -61,6 +61,11 @@ _SIGS = {
     "qhead_q6k_gemv": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "qhead_q6k": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "qhead_quantize_fp8_rows": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
+    "qhead_quantize_nvfp4_rows": (ctypes.c_int, [_vp, _i32, _i32, _f32, _vp, _vp, _vp]),
+    "qhead_quantize_q6k_rows": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
+    "qhead_dequant_nvfp4_bf16": (ctypes.c_int, [_vp, _vp, _i32, _i32, _f32, _vp, _vp]),
+    "qhead_dequant_fp4_e8m0_bf16": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, ctypes.c_int64, _vp,
+                                                   _vp]),
 }
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -262,3 +267,60 @@ def quantize_fp8_rows(w_f32: torch.Tensor, codes=None, scales=None, stream=None)
                                       _stream(stream))
     _check(st, "qhead_quantize_fp8_rows")
     return codes, scales
+
+
+def quantize_nvfp4_rows(w_f32: torch.Tensor, global_scale: float, w_packed=None,
+                        block_scale=None, stream=None):
+    """Load-time NVFP4 quantization of F32 weights with global multiplier g:
+    (w_packed uint8 [vocab, hidden/2], block_scale uint8 [vocab, hidden/16])."""
+    vocab, hidden = w_f32.shape
+    if w_packed is None:
+        w_packed = torch.empty((vocab, hidden // 2), dtype=torch.uint8, device=w_f32.device)
+    if block_scale is None:
+        block_scale = torch.empty((vocab, hidden // 16), dtype=torch.uint8, device=w_f32.device)
+    st = _lib.qhead_quantize_nvfp4_rows(_dev(w_f32, "w_f32", _F32), vocab, hidden,
+                                        float(global_scale), _dev(w_packed, "w_packed", _U8),
+                                        _dev(block_scale, "block_scale", _U8), _stream(stream))
+    _check(st, "qhead_quantize_nvfp4_rows")
+    return w_packed, block_scale
+
+
+def quantize_q6k_rows(w_f32: torch.Tensor, blocks=None, stream=None) -> torch.Tensor:
+    """Load-time Q6_K quantization of F32 weights: uint8 [vocab, hidden/256*210]."""
+    vocab, hidden = w_f32.shape
+    if blocks is None:
+        blocks = torch.empty((vocab, hidden // 256 * Q6K_BLOCK_BYTES), dtype=torch.uint8,
+                             device=w_f32.device)
+    st = _lib.qhead_quantize_q6k_rows(_dev(w_f32, "w_f32", _F32), vocab, hidden,
+                                      _dev(blocks, "blocks", _U8), _stream(stream))
+    _check(st, "qhead_quantize_q6k_rows")
+    return blocks
+
+
+def dequant_nvfp4_bf16(w_packed, block_scale, global_scale: float, out=None,
+                       stream=None) -> torch.Tensor:
+    """Load-time NVFP4 -> BF16: bf16 [rows, cols] from w_packed [rows, cols/2]."""
+    rows = w_packed.shape[0]
+    cols = w_packed.shape[1] * 2
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=w_packed.device)
+    st = _lib.qhead_dequant_nvfp4_bf16(_dev(w_packed, "w_packed", _U8),
+                                       _dev(block_scale, "block_scale", _U8), rows, cols,
+                                       float(global_scale), _dev(out, "out", _BF16),
+                                       _stream(stream))
+    _check(st, "qhead_dequant_nvfp4_bf16")
+    return out
+
+
+def dequant_fp4_e8m0_bf16(w_packed, scale_e8m0, out=None, stream=None) -> torch.Tensor:
+    """Load-time E2M1 + E8M0 group scales -> BF16 over the flat tensor
+    (total = 2 * w_packed.numel() values in scale_e8m0.numel() equal groups)."""
+    total = w_packed.numel() * 2
+    if out is None:
+        out = torch.empty((total,), dtype=torch.bfloat16, device=w_packed.device)
+    st = _lib.qhead_dequant_fp4_e8m0_bf16(_dev(w_packed, "w_packed", _U8),
+                                          _dev(scale_e8m0, "scale_e8m0", _U8), total,
+                                          scale_e8m0.numel(), _dev(out, "out", _BF16),
+                                          _stream(stream))
+    _check(st, "qhead_dequant_fp4_e8m0_bf16")
+    return out

@@ -303,6 +303,58 @@ int qhead_q6k(const uint8_t* blocks, const void* scales, const uint16_t* x_bf16,
     return QHEAD_OK;
 }
 
+int qhead_quantize_nvfp4_rows(const float* w_f32, int32_t vocab, int32_t hidden,
+                              float global_scale, uint8_t* w_packed, uint8_t* block_scale,
+                              void* stream) {
+    if (hidden <= 0 || vocab < 0 || hidden % 16) return QHEAD_ERR_SHAPE;
+    if (vocab == 0) return QHEAD_OK;
+    if (!w_f32 || !w_packed || !block_scale) return QHEAD_ERR_NULL;
+    if (!aligned(w_f32, 16) || !aligned(w_packed, 8)) return QHEAD_ERR_ALIGN;
+    DeviceInfo dev;
+    if (int st = device_or_error(&dev)) return st;
+    return hip_status(run_quantize_nvfp4_rows(w_f32, vocab, hidden, global_scale, w_packed,
+                                              block_scale, static_cast<hipStream_t>(stream)));
+}
+
+int qhead_quantize_q6k_rows(const float* w_f32, int32_t vocab, int32_t hidden, uint8_t* blocks,
+                            void* stream) {
+    if (hidden <= 0 || vocab < 0 || hidden % 256) return QHEAD_ERR_SHAPE;
+    if (vocab == 0) return QHEAD_OK;
+    if (!w_f32 || !blocks) return QHEAD_ERR_NULL;
+    if (!aligned(w_f32, 16) || !aligned(blocks, 2)) return QHEAD_ERR_ALIGN;
+    DeviceInfo dev;
+    if (int st = device_or_error(&dev)) return st;
+    return hip_status(
+        run_quantize_q6k_rows(w_f32, vocab, hidden, blocks, static_cast<hipStream_t>(stream)));
+}
+
+int qhead_dequant_nvfp4_bf16(const uint8_t* w_packed, const uint8_t* block_scale, int32_t rows,
+                             int32_t cols, float global_scale, uint16_t* out_bf16, void* stream) {
+    if (rows < 0 || cols <= 0 || cols % 32) return QHEAD_ERR_SHAPE;
+    if (rows == 0) return QHEAD_OK;
+    if (!w_packed || !block_scale || !out_bf16) return QHEAD_ERR_NULL;
+    if (!aligned(w_packed, 16) || !aligned(block_scale, 2) || !aligned(out_bf16, 16))
+        return QHEAD_ERR_ALIGN;
+    DeviceInfo dev;
+    if (int st = device_or_error(&dev)) return st;
+    return hip_status(run_dequant_nvfp4_bf16(w_packed, block_scale, global_scale, rows, cols,
+                                             out_bf16, dev, static_cast<hipStream_t>(stream)));
+}
+
+int qhead_dequant_fp4_e8m0_bf16(const uint8_t* w_packed, const uint8_t* scale_e8m0, int64_t total,
+                                int64_t num_groups, uint16_t* out_bf16, void* stream) {
+    if (total < 0 || num_groups <= 0) return QHEAD_ERR_SHAPE;
+    if (total % num_groups) return QHEAD_ERR_SHAPE;
+    if ((total / num_groups) % 16) return QHEAD_ERR_SHAPE;
+    if (total == 0) return QHEAD_OK;
+    if (!w_packed || !scale_e8m0 || !out_bf16) return QHEAD_ERR_NULL;
+    if (!aligned(w_packed, 8) || !aligned(out_bf16, 16)) return QHEAD_ERR_ALIGN;
+    DeviceInfo dev;
+    if (int st = device_or_error(&dev)) return st;
+    return hip_status(run_dequant_fp4_e8m0_bf16(w_packed, scale_e8m0, total, total / num_groups,
+                                                out_bf16, dev, static_cast<hipStream_t>(stream)));
+}
+
 int qhead_quantize_fp8_rows(const float* w_f32, int32_t vocab, int32_t hidden, uint8_t* w_e4m3,
                             float* row_scale, void* stream) {
     if (hidden <= 0 || vocab < 0 || hidden % 16) return QHEAD_ERR_SHAPE;

@@ -28,6 +28,17 @@ hipError_t run_quant_act_e4m3(const uint16_t* x, int rows, int H, uint8_t* xq, f
 hipError_t run_quant_q8_1(const uint16_t* x, int rows, int H, uint8_t* q8, hipStream_t stream);
 hipError_t run_quantize_fp8_rows(const float* w, int V, int H, uint8_t* codes, float* scales,
                                  hipStream_t stream);
+hipError_t run_quantize_nvfp4_rows(const float* w, int64_t V, int H, float g, uint8_t* packed,
+                                   uint8_t* bs, hipStream_t stream);
+hipError_t run_quantize_q6k_rows(const float* w, int64_t V, int H, uint8_t* blocks,
+                                 hipStream_t stream);
+
+// Load-time FP4 -> BF16 dequantization.
+hipError_t run_dequant_nvfp4_bf16(const uint8_t* wp, const uint8_t* bs, float g, int64_t n, int k,
+                                  uint16_t* out, const DeviceInfo& dev, hipStream_t stream);
+hipError_t run_dequant_fp4_e8m0_bf16(const uint8_t* wp, const uint8_t* scales, int64_t total,
+                                     int64_t block, uint16_t* out, const DeviceInfo& dev,
+                                     hipStream_t stream);
 
 // NVFP4 (1 <= R <= 8) and Q6_K (1 <= R <= 8).
 hipError_t run_nvfp4(const uint8_t* Wp, const uint8_t* bs, const uint16_t* x, float g, int R,

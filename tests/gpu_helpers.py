@@ -75,5 +75,22 @@ def fp8_head(cfg_index: int):
     return codes, scales, dev_u8(codes), dev_f32(scales)
 
 
+@functools.lru_cache(maxsize=1)
+def nvfp4_head():
+    """Host (packed, block scales, g) and device copies of the full NVFP4 head
+    of the 129280 x 7168 config."""
+    log("[prep] nvfp4 head cfg4")
+    wp, bs, g = oracle.prep_config_weights(4, "nvfp4")
+    return wp, bs, g, dev_u8(wp), dev_u8(bs)
+
+
+@functools.lru_cache(maxsize=1)
+def q6k_head():
+    """Host and device copies of the full Q6_K head of the 129280 x 7168 config."""
+    log("[prep] q6k head cfg4")
+    blocks = oracle.prep_config_weights(4, "q6k")
+    return blocks, dev_u8(blocks)
+
+
 def x_rows(cfg_index: int, rows: int, **kw) -> np.ndarray:
     return synth.activations_bf16(cfg_index, rows, **kw)

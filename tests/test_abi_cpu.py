@@ -31,7 +31,7 @@ MIS = 0x10001
 
 def test_exports_every_declared_function(qh):
     names = qh.header_functions()
-    assert len(names) == 14
+    assert len(names) == 18
     for n in names:
         assert hasattr(qh.lib(), n), n
     out = subprocess.run(["nm", "-D", "--defined-only", qh.LIB_PATH], capture_output=True,
@@ -136,6 +136,42 @@ def test_quantize_fp8_rows_validation(qh):
     assert f(A16, 8, 24, A16, A16, None) == -2
     assert f(A16 + 4, 8, 16, A16, A16, None) == -3
     assert f(A16, 0, 16, A16, A16, None) == 0
+
+
+def test_quantize_nvfp4_q6k_rows_validation(qh):
+    L = qh.lib()
+    f = L.qhead_quantize_nvfp4_rows
+    assert f(A16, 8, 24, 1.0, A16, A16, None) == -2      # hidden % 16
+    assert f(A16, -1, 32, 1.0, A16, A16, None) == -2
+    assert f(A16, 8, 32, 1.0, A16, None, None) == -1
+    assert f(A16 + 4, 8, 32, 1.0, A16, A16, None) == -3
+    assert f(A16, 8, 32, 1.0, A16 + 4, A16, None) == -3
+    assert f(None, 0, 32, 1.0, None, None, None) == 0    # vocab = 0: no launch
+    g = L.qhead_quantize_q6k_rows
+    assert g(A16, 8, 384, A16, None) == -2              # hidden % 256
+    assert g(A16, 8, 256, None, None) == -1
+    assert g(A16, 8, 256, A16 + 1, None) == -3
+    assert g(None, 0, 256, None, None) == 0
+
+
+def test_dequant_validation(qh):
+    L = qh.lib()
+    f = L.qhead_dequant_nvfp4_bf16
+    assert f(A16, A16, 4, 48, 1.0, A16, None) == -2      # cols % 32
+    assert f(A16, A16, -1, 64, 1.0, A16, None) == -2
+    assert f(A16, None, 4, 64, 1.0, A16, None) == -1
+    assert f(A16 + 8, A16, 4, 64, 1.0, A16, None) == -3
+    assert f(A16, A16 + 1, 4, 64, 1.0, A16, None) == -3
+    assert f(A16, A16, 4, 64, 1.0, A16 + 2, None) == -3
+    assert f(None, None, 0, 64, 1.0, None, None) == 0
+    g = L.qhead_dequant_fp4_e8m0_bf16
+    assert g(A16, A16, 96, 5, A16, None) == -2           # 96 values do not split in 5 groups
+    assert g(A16, A16, 96, 4, A16, None) == -2           # groups of 24 (not a multiple of 16)
+    assert g(A16, A16, 96, 0, A16, None) == -2
+    assert g(A16, A16, 96, 3, None, None) == -1
+    assert g(A16 + 4, A16, 96, 3, A16, None) == -3
+    assert g(A16, A16, 96, 3, A16 + 8, None) == -3
+    assert g(None, None, 0, 3, None, None) == 0
 
 
 def test_binding_rejects_host_tensors(qh):

@@ -6,8 +6,6 @@ bit-exact; one-hot decodes and exact dyadic cases bit-exact; row-invariant
 bits across row counts and chunkings.
 """
 
-import functools
-
 import numpy as np
 import pytest
 import torch
@@ -15,7 +13,7 @@ import torch
 import oracle
 import synth
 from gpu_helpers import (DEV, assert_within_bound, bf16_bits_to_f64, dev_bf16, dev_u8, host_bits,
-                         log, sample_vidx)
+                         log, nvfp4_head, q6k_head, sample_vidx)
 
 pytestmark = pytest.mark.gpu
 
@@ -92,15 +90,8 @@ def test_nvfp4_zero_global_scale(qh):
     assert (bf16_bits_to_f64(out) == 0).all()
 
 
-@functools.lru_cache(maxsize=1)
-def _cfg4_nvfp4():
-    log("[prep] nvfp4 head cfg4")
-    wp, bs, g = oracle.prep_config_weights(4, "nvfp4")
-    return wp, bs, g, dev_u8(wp), dev_u8(bs)
-
-
 def test_nvfp4_cfg4_full_head(qh):
-    wp, bs, g, wpd, bsd = _cfg4_nvfp4()
+    wp, bs, g, wpd, bsd = nvfp4_head()
     cfg = synth.CONFIGS[4]
     x = synth.activations_bf16(4, 8)
     vidx = sample_vidx(cfg.vocab, 1500, 4)
@@ -188,15 +179,8 @@ def test_q6k_edge_shapes_and_alignment(qh):
         assert np.array_equal(host_bits(out2), host_bits(out))
 
 
-@functools.lru_cache(maxsize=1)
-def _cfg4_q6k():
-    log("[prep] q6k head cfg4")
-    blocks = oracle.prep_config_weights(4, "q6k")
-    return blocks, dev_u8(blocks)
-
-
 def test_q6k_cfg4_full_head(qh):
-    blocks, bd = _cfg4_q6k()
+    blocks, bd = q6k_head()
     cfg = synth.CONFIGS[4]
     x = synth.activations_bf16(4, 8)
     q8 = oracle.quant_q8_1(x)
