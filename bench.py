@@ -1,19 +1,26 @@
-"""Benchmark: achieved HBM GB/s and logits rows/s of the FP8 E4M3 LM head.
+"""Benchmark: achieved HBM GB/s and logits rows/s of the quantized LM head.
 
-Workload (default): the 1.27 GB FP8 head -- vocab 155136 x hidden 8192 E4M3
-weights (N(0, 0.015) draws quantized per row on the device, F32 row scales),
-BF16 activations from N(0, 1) -- decoded at rows 1, 2, 4, 8 and 16. One step
-is one pass of the head path over that batch: five qhead_fp8_rowscale calls,
-each one weight pass. The weights are resident in HBM before timing starts.
+Workload (default, --workload fp8): the 1.27 GB FP8 head -- vocab 155136 x
+hidden 8192 E4M3 weights (N(0, 0.015) draws quantized per row on the device,
+F32 row scales), BF16 activations from N(0, 1) -- decoded at rows 1, 2, 4, 8
+and 16. One step is one pass of the head path over that batch: five
+qhead_fp8_rowscale calls, each one weight pass. The weights are resident in
+HBM before timing starts.
 
-value = algorithmic bytes of the step / step time, where a launch's
-algorithmic bytes are W + row scales + R * (2 * hidden + 2 * vocab) (weights
-once per launch, activations in, logits out). Launch durations come from HIP
-events recorded on the launch stream around every call.
+value = algorithmic bytes of the step / step time, where a call's
+algorithmic bytes are the weight bytes once plus R * (2 * hidden + 2 * vocab)
+(activations in, logits out) plus, for W8A8 and Q6_K, the quantized
+activations written and read back once. Call durations come from HIP events
+recorded on the launch stream around every call.
 
-Prints one JSON line (see the repository's design notes for field meanings).
-Other workloads for local measurements: --workload w8a8 (the 129280 x 7168
-head, W8A8 at rows 1 and 16) or --rows to change the row sweep.
+Other workloads, each on the 129280 x 7168 head (N(0, 0.02) weights
+quantized on the device):
+  --workload w8a8     W8A8 calls of 1, 16 and 128 rows (activation
+                      quantization + GEMV per call)
+  --workload nvfp4    NVFP4 W4A16 at rows 1, 2, 4, 8
+  --workload q6k      Q6_K with q8_1 activations at rows 1, 2, 4, 8
+  --workload dequant  load-time NVFP4 -> BF16 of the whole head
+--rows changes the row sweep. Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -24,6 +31,7 @@ import json
 import os
 import sys
 import time
+from dataclasses import dataclass
 
 import numpy as np
 
@@ -31,15 +39,57 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "fp8_gemv_155136x8192_counters.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "quantized_weight_decode_amd", "csrc", f)
-                  for f in ("fp8_gemv.hip", "qhead_device.h")]
+CSRC = os.path.join(ROOT, "quantized_weight_decode_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash() -> str:
+@dataclass(frozen=True)
+class Workload:
+    cfg: int
+    rows: str
+    kernel: str
+    sources: tuple
+    counters: str
+    metric: str
+    dtype: str
+    data: str
+
+
+_W002 = "synthetic (seeded N(0,0.02) weights quantized on the device, N(0,1) BF16 x)"
+WORKLOADS = {
+    "fp8": Workload(
+        2, "1,2,4,8,16", "fp8_gemv_kernel", ("fp8_gemv.hip", "qhead_device.h"),
+        "fp8_gemv_155136x8192_counters.json",
+        "achieved HBM GB/s (% of peak) & logits rows/sec, 1.27 GB FP8 head, rows 1..16",
+        "fp8e4m3 x bf16 -> f32 acc, bf16 out",
+        "synthetic (seeded N(0,0.015) weights quantized per row to E4M3, N(0,1) BF16 x)"),
+    "w8a8": Workload(
+        3, "1,16,128", "fp8_gemv_kernel<W8A8> + quant_act_e4m3_kernel (per call)",
+        ("fp8_gemv.hip", "quant.hip", "qhead_device.h"), "w8a8_129280x7168_counters.json",
+        "achieved HBM GB/s, W8A8 head 129280x7168, calls of 1/16/128 rows",
+        "fp8e4m3 x fp8e4m3 -> f32 acc, bf16 out", _W002),
+    "nvfp4": Workload(
+        4, "1,2,4,8", "nvfp4_gemv_kernel", ("nvfp4_gemv.hip", "qhead_device.h"),
+        "nvfp4_gemv_129280x7168_counters.json",
+        "achieved HBM GB/s, NVFP4 W4A16 head 129280x7168, rows 1..8",
+        "e2m1 x e4m3 block scale x bf16 -> f32 acc, bf16 out", _W002),
+    "q6k": Workload(
+        4, "1,2,4,8", "q6k_gemv_kernel + quant_q8_1_kernel (per call)",
+        ("q6k_gemv.hip", "quant.hip", "qhead_device.h"), "q6k_gemv_129280x7168_counters.json",
+        "achieved HBM GB/s, Q6_K head 129280x7168 with q8_1 activations, rows 1..8",
+        "int6 x int8 -> i32 dot4, f32 scales, bf16 out", _W002),
+    "dequant": Workload(
+        4, "0", "dequant_nvfp4_bf16_kernel", ("dequant.hip", "qhead_device.h"),
+        "dequant_nvfp4_129280x7168_counters.json",
+        "achieved HBM GB/s, load-time NVFP4 -> BF16 of the 129280x7168 head",
+        "e2m1 x e4m3 x f32 global -> bf16", _W002),
+}
+
+
+def kernel_source_hash(wl: Workload) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
+    for name in wl.sources:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -49,8 +99,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--rows", type=str, default="1,2,4,8,16")
-    ap.add_argument("--workload", choices=["fp8", "w8a8"], default="fp8")
+    ap.add_argument("--rows", type=str, default=None)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="fp8")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target duration of the oracle CPU baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -60,67 +110,105 @@ def parse():
     return ap.parse_args()
 
 
-def build_head(cfg_index: int, qh, torch):
+def nvfp4_global(amax: float) -> float:
+    """The head's NVFP4 global multiplier: fl32(amax / 2688), 2688 = 6 * 448."""
+    return float(np.float32(amax) / np.float32(2688.0))
+
+
+def build_head(name: str, cfg, qh, torch):
     """Generate the seeded head chunk by chunk and quantize it on the device."""
     import synth
 
-    cfg = synth.CONFIGS[cfg_index]
     dev = torch.device("cuda:0")
-    codes = torch.empty((cfg.vocab, cfg.hidden), dtype=torch.uint8, device=dev)
-    scales = torch.empty((cfg.vocab,), dtype=torch.float32, device=dev)
-    for lo, hi, wf in synth.iter_weight_chunks(cfg_index):
-        wd = torch.from_numpy(wf).to(dev)
-        qh.quantize_fp8_rows(wd, codes=codes[lo:hi], scales=scales[lo:hi])
-        del wd
+    V, H = cfg.vocab, cfg.hidden
+    if name in ("fp8", "w8a8"):
+        codes = torch.empty((V, H), dtype=torch.uint8, device=dev)
+        scales = torch.empty((V,), dtype=torch.float32, device=dev)
+        for lo, hi, wf in synth.iter_weight_chunks(cfg.index):
+            wd = torch.from_numpy(wf).to(dev)
+            qh.quantize_fp8_rows(wd, codes=codes[lo:hi], scales=scales[lo:hi])
+            del wd
+        torch.cuda.synchronize()
+        return {"codes": codes, "scales": scales}
+    wf = torch.empty((V, H), dtype=torch.float32, device=dev)
+    for lo, hi, chunk in synth.iter_weight_chunks(cfg.index):
+        wf[lo:hi].copy_(torch.from_numpy(chunk))
+    if name == "q6k":
+        head = {"blocks": qh.quantize_q6k_rows(wf)}
+    else:
+        g = nvfp4_global(float(wf.abs().max().item()))
+        wp, bs = qh.quantize_nvfp4_rows(wf, g)
+        head = {"wp": wp, "bs": bs, "g": g}
     torch.cuda.synchronize()
-    return cfg, codes, scales
+    del wf
+    torch.cuda.empty_cache()
+    return head
 
 
-def algorithmic_bytes(fmt: str, V: int, H: int, R: int) -> int:
-    w = V * H + 4 * V
-    act = R * (2 * H + 2 * V)
-    if fmt == "w8a8":
-        # quantized activations written and read back once per call
-        act += 2 * R * (H + 4)
-    return w + act
+def algorithmic_bytes(name: str, V: int, H: int, R: int) -> int:
+    """Bytes one call must move: weights once, activations in, logits out,
+    and quantized activations written and read back where the format has them."""
+    io = R * (2 * H + 2 * V)
+    if name == "fp8":
+        return V * H + 4 * V + io
+    if name == "w8a8":
+        return V * H + 4 * V + io + 2 * R * (H + 4)
+    if name == "nvfp4":
+        return V * H // 2 + V * H // 16 + io
+    if name == "q6k":
+        return V * (H // 256) * 210 + io + 2 * R * (H // 32) * 36
+    if name == "dequant":
+        return V * H // 2 + V * H // 16 + 2 * V * H
+    raise ValueError(name)
 
 
-def cpu_baseline(cfg_index: int, rows: list[int], target_s: float):
+def cpu_baseline(name: str, cfg, rows: list[int], target_s: float):
     """The oracle timed on a bounded sample of the same workload (vocab rows
     [0, n) of the same head, the same row sweep); returns GB/s of that sample
     in the workload's algorithmic bytes."""
     import oracle
     import synth
 
-    cfg = synth.CONFIGS[cfg_index]
-    x = synth.activations_bf16(cfg_index, max(rows), max_rows=max(rows))
+    x = synth.activations_bf16(cfg.index, max(max(rows), 1), max_rows=max(max(rows), 1))
 
     def run(n: int) -> float:
-        wf = synth.weight_rows_f32(cfg_index, 0, n)
-        w, s = oracle.prep_fp8_rows(wf)
+        wf = synth.weight_rows_f32(cfg.index, 0, n)
         vidx = np.arange(n, dtype=np.int64)
+        if name in ("fp8", "w8a8"):
+            w, s = oracle.prep_fp8_rows(wf)
+        elif name == "q6k":
+            blocks = oracle.prep_q6k_rows(wf)
+        else:
+            g = oracle.nvfp4_global(float(np.abs(wf).max()))
+            wp, bs = oracle.prep_nvfp4_rows(wf, g)
         t0 = time.perf_counter()
         for R in rows:
-            if cfg.fmt == "w8a8":
+            if name == "fp8":
+                oracle.fp8_rowscale_ref(w, s, x[:R], vidx)
+            elif name == "w8a8":
                 xq, sa = oracle.quant_act_e4m3(x[:R])
                 oracle.w8a8_ref(w, s, xq, sa, vidx)
+            elif name == "nvfp4":
+                oracle.nvfp4_ref(wp, bs, g, x[:R], vidx)
+            elif name == "q6k":
+                oracle.q6k_ref(blocks, oracle.quant_q8_1(x[:R]), cfg.hidden, vidx)
             else:
-                oracle.fp8_rowscale_ref(w, s, x[:R], vidx)
+                oracle.dequant_nvfp4_bf16(wp, bs, g)
         return time.perf_counter() - t0
 
     n = 256
     t = run(n)
     n = int(min(cfg.vocab, max(n, n * target_s / max(t, 1e-3))))
     t = run(n)
-    fmt = "w8a8" if cfg.fmt == "w8a8" else "fp8"
-    bytes_ = sum(algorithmic_bytes(fmt, n, cfg.hidden, R) for R in rows)
+    bytes_ = sum(algorithmic_bytes(name, n, cfg.hidden, R) for R in rows)
+    what = "NVFP4 -> BF16 of those rows" if name == "dequant" else f"rows {rows}"
     return {
         "value": round(bytes_ / t / 1e9, 4),
         "unit": "GB/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"vocab rows [0, {n}) of the same head, rows {rows}, {t:.1f} s "
-                  f"(binary64 dequantize-then-dot, OpenMP)",
+        "sample": f"vocab rows [0, {n}) of the same head, {what}, {t:.1f} s "
+                  f"(binary64 oracle, OpenMP)",
         "rows_per_s_full_head": round(sum(rows) * n / cfg.vocab / t, 6),
     }
 
@@ -147,26 +235,44 @@ def main():
         return
 
     import quantized_weight_decode_amd as qh
-
-    rows = [int(r) for r in args.rows.split(",")]
-    cfg_index = 2 if args.workload == "fp8" else 3
-    t_prep = time.perf_counter()
-    cfg, codes, scales = build_head(cfg_index, qh, torch)
-    t_prep = time.perf_counter() - t_prep
-    V, H = cfg.vocab, cfg.hidden
     import synth
 
-    xall = synth.activations_bf16(cfg_index, max(rows), max_rows=max(rows))
+    name = args.workload
+    wl = WORKLOADS[name]
+    cfg = synth.CONFIGS[wl.cfg]
+    rows = [int(r) for r in (args.rows or wl.rows).split(",")]
+    if name == "dequant":
+        rows = [0]
+    t_prep = time.perf_counter()
+    head = build_head(name, cfg, qh, torch)
+    t_prep = time.perf_counter() - t_prep
+    V, H = cfg.vocab, cfg.hidden
+
     dev = torch.device("cuda:0")
+    nx = max(max(rows), 1)
+    xall = synth.activations_bf16(cfg.index, nx, max_rows=nx)
     xs = {R: torch.from_numpy(xall[:R].view(np.int16)).to(dev).view(torch.bfloat16) for R in rows}
-    outs = {R: torch.empty((R, V), dtype=torch.bfloat16, device=dev) for R in rows}
-    ws = qh.w8a8_workspace(H, dev) if args.workload == "w8a8" else None
+    if name == "dequant":
+        outs = {0: torch.empty((V, H), dtype=torch.bfloat16, device=dev)}
+    else:
+        outs = {R: torch.empty((R, V), dtype=torch.bfloat16, device=dev) for R in rows}
+    ws = None
+    if name == "w8a8":
+        ws = qh.w8a8_workspace(H, dev)
+    elif name == "q6k":
+        ws = torch.empty((qh.q6k_workspace_bytes(H),), dtype=torch.uint8, device=dev)
 
     def call(R):
-        if args.workload == "w8a8":
-            qh.w8a8(codes, scales, xs[R], out=outs[R], workspace=ws)
+        if name == "fp8":
+            qh.fp8_rowscale(head["codes"], head["scales"], xs[R], out=outs[R])
+        elif name == "w8a8":
+            qh.w8a8(head["codes"], head["scales"], xs[R], out=outs[R], workspace=ws)
+        elif name == "nvfp4":
+            qh.nvfp4(head["wp"], head["bs"], xs[R], head["g"], out=outs[R])
+        elif name == "q6k":
+            qh.q6k(head["blocks"], xs[R], out=outs[R], workspace=ws)
         else:
-            qh.fp8_rowscale(codes, scales, xs[R], out=outs[R])
+            qh.dequant_nvfp4_bf16(head["wp"], head["bs"], head["g"], out=outs[0])
 
     for _ in range(args.warmup):
         for R in rows:
@@ -192,33 +298,43 @@ def main():
 
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    per_rows = {}
-    for i, R in enumerate(rows):
-        d = np.array([evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(args.steps)])
-        b = algorithmic_bytes(args.workload, V, H, R)
-        per_rows[str(R)] = {"us_median": round(float(np.median(d)) * 1e3, 2),
-                            "us_min": round(float(d.min()) * 1e3, 2),
-                            "GBps": round(b / (np.median(d) * 1e-3) / 1e9, 1),
-                            "pct_peak": round(b / (np.median(d) * 1e-3) / 1e9 / HBM_PEAK_GBS * 100,
-                                              1),
-                            "rows_per_s": round(R / (np.median(d) * 1e-3), 1)}
-    step_bytes = sum(algorithmic_bytes(args.workload, V, H, R) for R in rows)
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
     launch_ms = np.array([[evs[k][i][0].elapsed_time(evs[k][i][1]) for i in range(len(rows))]
                           for k in range(args.steps)])
+    per_rows = {}
+    for i, R in enumerate(rows):
+        d = launch_ms[:, i]
+        b = algorithmic_bytes(name, V, H, R)
+        gbs = b / (np.median(d) * 1e-3) / 1e9
+        per_rows["head" if name == "dequant" else str(R)] = {
+            "us_median": round(float(np.median(d)) * 1e3, 2),
+            "us_min": round(float(d.min()) * 1e3, 2),
+            "GBps": round(gbs, 1),
+            "pct_peak": round(gbs / HBM_PEAK_GBS * 100, 1),
+            "rows_per_s": round(R / (np.median(d) * 1e-3), 1)}
+    step_bytes = sum(algorithmic_bytes(name, V, H, R) for R in rows)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
     mean_launch_bytes = step_bytes / len(rows)
     achieved = mean_launch_bytes / (launch_ms.mean() * 1e-3) / 1e9
 
     traffic = None
-    if os.path.exists(PROFILE_COUNTERS) and args.workload == "fp8" and rows == [1, 2, 4, 8, 16]:
-        with open(PROFILE_COUNTERS) as f:
+    counters = os.path.join(PROFILES, wl.counters)
+    if os.path.exists(counters) and rows == [int(r) for r in wl.rows.split(",")]:
+        with open(counters) as f:
             prof = json.load(f)
-        if prof.get("kernel_source_hash") == kernel_source_hash():
+        if prof.get("kernel_source_hash") == kernel_source_hash(wl):
             traffic = prof.get("hbm_bytes_per_launch")
 
+    config = {"workload": cfg.label if name != "dequant" else
+              f"nvfp4 -> bf16 dequant of the {V}x{H} head",
+              "vocab": V, "hidden": H, "rows_per_step": rows if name != "dequant" else [],
+              "launches_per_step": len(rows), "weight_bytes": algorithmic_bytes(name, V, H, 0),
+              "pct_of_hbm_peak": round(value / HBM_PEAK_GBS * 100, 2),
+              "per_rows": per_rows, "wall_s_timed": round(wall, 3),
+              "head_prep_s": round(t_prep, 1)}
+    if name != "dequant":
+        config["rows_per_s"] = round(sum(rows) / (ms_per_step * 1e-3), 1)
     line = {
-        "metric": "achieved HBM GB/s (% of peak) & logits rows/sec, 1.27 GB FP8 head, rows 1..16"
-        if args.workload == "fp8" else "achieved HBM GB/s, W8A8 head 129280x7168",
+        "metric": wl.metric,
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -228,23 +344,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3 x bf16 -> f32 acc, bf16 out" if args.workload == "fp8"
-        else "fp8e4m3 x fp8e4m3 -> f32 acc, bf16 out",
-        "data": "synthetic (seeded N(0,0.015) weights quantized per row to E4M3, N(0,1) BF16 x)",
-        "config": {"workload": cfg.label, "vocab": V, "hidden": H, "rows_per_step": rows,
-                   "launches_per_step": len(rows), "weight_bytes": V * H,
-                   "pct_of_hbm_peak": round(value / HBM_PEAK_GBS * 100, 2),
-                   "rows_per_s": round(sum(rows) / (ms_per_step * 1e-3), 1),
-                   "per_rows": per_rows, "wall_s_timed": round(wall, 3),
-                   "head_prep_s": round(t_prep, 1)},
+        "dtype": wl.dtype,
+        "data": wl.data,
+        "config": config,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "fp8_gemv_kernel (mean over the step's launches)",
+                     "kernel": f"{wl.kernel} (mean over the step's calls)",
                      "avg_launch_us": round(float(launch_ms.mean()) * 1e3, 2)},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg_index, rows, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(name, cfg, rows, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 
