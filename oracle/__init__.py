@@ -92,6 +92,9 @@ def lib():
             "orc_dequant_nvfp4_bf16": (None, [u8p, u8p, ctypes.c_float, i64, i32, u16p]),
             "orc_e8m0": (ctypes.c_double, [ctypes.c_uint8]),
             "orc_dequant_fp4_e8m0_bf16": (None, [u8p, u8p, i64, i64, u16p]),
+            "orc_silu_mul_bf16": (ctypes.c_uint16, [ctypes.c_uint16, ctypes.c_uint16]),
+            "orc_silu_mul_ambiguous": (ctypes.c_int, [ctypes.c_uint16, ctypes.c_uint16]),
+            "orc_quant_act_silu_e4m3": (i64, [u16p, u16p, i32, i32, i32, u8p, f32p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -173,6 +176,32 @@ def quant_act_e4m3(x_bf16: np.ndarray):
     lib().orc_quant_act_e4m3(_ptr(x, ctypes.c_uint16), rows, hidden, _ptr(xq, ctypes.c_uint8),
                              _ptr(sa, ctypes.c_float))
     return xq, sa
+
+
+def silu_mul_bf16(g_bits: int, u_bits: int) -> int:
+    """bf16(silu(g) * u) from BF16 bit patterns, silu and product in binary64."""
+    return int(lib().orc_silu_mul_bf16(int(g_bits) & 0xFFFF, int(u_bits) & 0xFFFF))
+
+
+def silu_mul_ambiguous(g_bits: int, u_bits: int) -> bool:
+    return bool(lib().orc_silu_mul_ambiguous(int(g_bits) & 0xFFFF, int(u_bits) & 0xFFFF))
+
+
+def quant_act_silu_e4m3(gate_bf16: np.ndarray, up_bf16: np.ndarray, hidden: int | None = None):
+    """Per-row E4M3 quantization of bf16(silu(gate) * up) over the first
+    `hidden` columns of gate/up ([R, ld] BF16 bits). Returns (xq uint8 [R, hidden],
+    sa float32 [R], number of ambiguous elements)."""
+    g = np.ascontiguousarray(gate_bf16, dtype=np.uint16)
+    u = np.ascontiguousarray(up_bf16, dtype=np.uint16)
+    assert g.shape == u.shape
+    rows, ld = g.shape
+    hidden = ld if hidden is None else hidden
+    xq = np.empty((rows, hidden), dtype=np.uint8)
+    sa = np.empty(rows, dtype=np.float32)
+    amb = lib().orc_quant_act_silu_e4m3(_ptr(g, ctypes.c_uint16), _ptr(u, ctypes.c_uint16), ld,
+                                        rows, hidden, _ptr(xq, ctypes.c_uint8),
+                                        _ptr(sa, ctypes.c_float))
+    return xq, sa, int(amb)
 
 
 def quant_q8_1(x_bf16: np.ndarray) -> np.ndarray:

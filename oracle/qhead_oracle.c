@@ -40,6 +40,7 @@
 #include <math.h>
 #include <omp.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORC_API __attribute__((visibility("default")))
@@ -216,6 +217,49 @@ ORC_API void orc_quant_act_e4m3(const uint16_t* x, int rows, int hidden, uint8_t
             qr[k] = orc_enc_e4m3(t);
         }
     }
+}
+
+/* SiLU product of the FFN down projection ("w8a8_layer.rs", W8a8Ctx::silu_proj:
+ * the activation is bf16(silu(gate) * up), quantized per row in the same launch
+ * as the W8A8 activations are). The pages do not fix silu's precision; it is
+ * evaluated here in binary64, silu(g) = g / (1 + exp(-g)), times u, and the
+ * binary64 value is rounded once to BF16 (nearest even). */
+ORC_API uint16_t orc_silu_mul_bf16(uint16_t g_bits, uint16_t u_bits) {
+    double g = orc_bf16(g_bits), u = orc_bf16(u_bits);
+    double s = g / (1.0 + exp(-g));
+    return orc_bf16_rne(s * u);
+}
+
+/* 1 when the binary64 SiLU product lies so close to a BF16 rounding boundary
+ * that a last-bit difference in exp could change its BF16 rounding (the
+ * rounding of the value scaled by 1 -+ 2^-44 differs), else 0. */
+ORC_API int orc_silu_mul_ambiguous(uint16_t g_bits, uint16_t u_bits) {
+    double g = orc_bf16(g_bits), u = orc_bf16(u_bits);
+    double p = (g / (1.0 + exp(-g))) * u;
+    uint16_t b = orc_bf16_rne(p);
+    double eps = ldexp(1.0, -44);
+    return orc_bf16_rne(p * (1.0 - eps)) != b || orc_bf16_rne(p * (1.0 + eps)) != b;
+}
+
+/* Per-row E4M3 quantization of the SiLU product: p[r][k] =
+ * orc_silu_mul_bf16(gate[r*ld + k], up[r*ld + k]) for k < hidden, then the
+ * activation quantization above on p. Returns the number of ambiguous
+ * elements (see orc_silu_mul_ambiguous). */
+ORC_API int64_t orc_quant_act_silu_e4m3(const uint16_t* gate, const uint16_t* up, int ld,
+                                        int rows, int hidden, uint8_t* xq, float* sa) {
+    uint16_t* p = (uint16_t*)malloc((size_t)hidden * sizeof(uint16_t));
+    int64_t ambiguous = 0;
+    for (int r = 0; r < rows; r++) {
+        const uint16_t* gr = gate + (size_t)r * ld;
+        const uint16_t* ur = up + (size_t)r * ld;
+        for (int k = 0; k < hidden; k++) {
+            p[k] = orc_silu_mul_bf16(gr[k], ur[k]);
+            ambiguous += orc_silu_mul_ambiguous(gr[k], ur[k]);
+        }
+        orc_quant_act_e4m3(p, 1, hidden, xq + (size_t)r * hidden, sa + r);
+    }
+    free(p);
+    return ambiguous;
 }
 
 /* block_q8_1 quantization of BF16 rows ("lm_head_q6k.rs": hidden rows are

@@ -601,3 +601,71 @@ def test_prep_q6k_rows_nearest_levels():
             # decoded weights are the clamped nearest levels of the step grid
             q = np.clip(np.rint(w / step), -32, 31)
             assert np.array_equal(dec, q * step.astype(np.float64))
+
+
+# ------------------------------------------- SiLU product act-quant (FFN down)
+
+def test_silu_quant_worked_row():
+    rows = _rows("silu_quant_row.txt")
+    g = np.array([[int(r[0], 16) for r in rows]], dtype=np.uint16)
+    u = np.array([[int(r[1], 16) for r in rows]], dtype=np.uint16)
+    for r in rows:
+        assert oracle.silu_mul_bf16(int(r[0], 16), int(r[1], 16)) == int(r[2], 16), r
+    xq, sa, amb = oracle.quant_act_silu_e4m3(g, u)
+    assert amb == 0
+    assert sa[0] == np.float32(50) / np.float32(448)
+    assert [int(c) for c in xq[0]] == [int(r[3], 16) for r in rows]
+
+
+def _bf16_bits_of(v: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.asarray(v, dtype=np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+
+
+def test_silu_mul_matches_torch_silu():
+    # torch's float64 silu times u, rounded by the (separately pinned) BF16 rounding
+    rng = np.random.default_rng(21)
+    g = _bf16_bits_of(np.concatenate([rng.normal(0, 2, 3000), rng.normal(0, 30, 500),
+                                      [0.0, -0.0, 1e-30, -1e-30, 88.0, -88.0, 700.0]]))
+    u = _bf16_bits_of(rng.normal(0, 1.5, g.size))
+    gt = torch.from_numpy(bf16_bits_to_f64_local(g))
+    ut = torch.from_numpy(bf16_bits_to_f64_local(u))
+    ref = (torch.nn.functional.silu(gt) * ut).numpy()
+    for i in range(g.size):
+        want = oracle.bf16_rne(float(ref[i]))
+        got = oracle.silu_mul_bf16(int(g[i]), int(u[i]))
+        if oracle.silu_mul_ambiguous(int(g[i]), int(u[i])):
+            continue
+        assert got == want, (hex(int(g[i])), hex(int(u[i])), hex(got), hex(want))
+
+
+def bf16_bits_to_f64_local(bits):
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_silu_mul_exact_midpoint_is_flagged():
+    # silu(48) = 48 exactly in binary64 (1 + e^-48 rounds to 1); 48 * (1 + 2^-7)
+    # = 48.375 is the midpoint of 48.25 and 48.5, and ties go to the even 48.5
+    assert oracle.silu_mul_bf16(0x4240, 0x3F81) == 0x4242
+    assert oracle.silu_mul_ambiguous(0x4240, 0x3F81)
+    assert not oracle.silu_mul_ambiguous(0x3F80, 0x3F80)
+
+
+def test_quant_act_silu_strided_rows_and_zero_row():
+    rng = np.random.default_rng(22)
+    rows, hidden, ld = 5, 96, 112
+    g = _bf16_bits_of(rng.normal(0, 2, (rows, ld)))
+    u = _bf16_bits_of(rng.normal(0, 1, (rows, ld)))
+    u[3] = 0  # a row whose products are all zero (some -0)
+    xq, sa, amb = oracle.quant_act_silu_e4m3(g, u, hidden)
+    assert amb == 0 and xq.shape == (rows, hidden)
+    assert sa[3] == 0 and not xq[3].any()
+    p = np.array([[oracle.silu_mul_bf16(int(g[r, k]), int(u[r, k])) for k in range(hidden)]
+                  for r in range(rows)], dtype=np.uint16)
+    xq2, sa2 = oracle.quant_act_e4m3(p)
+    assert np.array_equal(xq, xq2) and np.array_equal(sa, sa2)
+    # columns past `hidden` do not matter
+    g2 = g.copy()
+    g2[:, hidden:] = 0x7F80
+    xq3, sa3, _ = oracle.quant_act_silu_e4m3(g2, u, hidden)
+    assert np.array_equal(xq, xq3) and np.array_equal(sa, sa3)
