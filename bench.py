@@ -20,6 +20,11 @@ quantized on the device):
   --workload nvfp4    NVFP4 W4A16 at rows 1, 2, 4, 8
   --workload q6k      Q6_K with q8_1 activations at rows 1, 2, 4, 8
   --workload dequant  load-time NVFP4 -> BF16 of the whole head
+  --workload w8a8_silu  W8A8 down projection of bf16(silu(gate) * up), output
+                      7168 x FFN width 18432, calls of 1, 16 and 128 rows;
+                      the calls rotate over 8 copies of the 132 MB weight
+                      (1.06 GB) so that no call finds its weight in the
+                      last-level cache, as when a decode step walks the layers
 --rows changes the row sweep. Prints one JSON line.
 """
 
@@ -41,6 +46,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "quantized_weight_decode_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
+SILU_WEIGHT_COPIES = 8
 
 
 @dataclass(frozen=True)
@@ -78,6 +84,13 @@ WORKLOADS = {
         ("q6k_gemv.hip", "quant.hip", "qhead_device.h"), "q6k_gemv_129280x7168_counters.json",
         "achieved HBM GB/s, Q6_K head 129280x7168 with q8_1 activations, rows 1..8",
         "int6 x int8 -> i32 dot4, f32 scales, bf16 out", _W002),
+    "w8a8_silu": Workload(
+        5, "1,16,128", "fp8_gemv_kernel<W8A8> + quant_act_silu_e4m3_kernel (per call)",
+        ("fp8_gemv.hip", "quant.hip", "qhead_device.h"), "w8a8_silu_7168x18432_counters.json",
+        "achieved HBM GB/s, W8A8 SiLU down projection 7168x18432, calls of 1/16/128 rows",
+        "bf16 silu(gate)*up -> fp8e4m3 x fp8e4m3 -> f32 acc, bf16 out",
+        "synthetic (seeded N(0,0.02) weights quantized per row on the device, gate N(0,1.5^2) "
+        "and up N(0,1) BF16)"),
     "dequant": Workload(
         4, "0", "dequant_nvfp4_bf16_kernel", ("dequant.hip", "qhead_device.h"),
         "dequant_nvfp4_129280x7168_counters.json",
@@ -121,7 +134,7 @@ def build_head(name: str, cfg, qh, torch):
 
     dev = torch.device("cuda:0")
     V, H = cfg.vocab, cfg.hidden
-    if name in ("fp8", "w8a8"):
+    if name in ("fp8", "w8a8", "w8a8_silu"):
         codes = torch.empty((V, H), dtype=torch.uint8, device=dev)
         scales = torch.empty((V,), dtype=torch.float32, device=dev)
         for lo, hi, wf in synth.iter_weight_chunks(cfg.index):
@@ -129,6 +142,11 @@ def build_head(name: str, cfg, qh, torch):
             qh.quantize_fp8_rows(wd, codes=codes[lo:hi], scales=scales[lo:hi])
             del wd
         torch.cuda.synchronize()
+        if name == "w8a8_silu":
+            copies = [(codes, scales)] + [(codes.clone(), scales.clone())
+                                          for _ in range(SILU_WEIGHT_COPIES - 1)]
+            torch.cuda.synchronize()
+            return {"copies": copies}
         return {"codes": codes, "scales": scales}
     wf = torch.empty((V, H), dtype=torch.float32, device=dev)
     for lo, hi, chunk in synth.iter_weight_chunks(cfg.index):
@@ -153,6 +171,9 @@ def algorithmic_bytes(name: str, V: int, H: int, R: int) -> int:
         return V * H + 4 * V + io
     if name == "w8a8":
         return V * H + 4 * V + io + 2 * R * (H + 4)
+    if name == "w8a8_silu":
+        # gate and up read (2 x 2 bytes per value) instead of one BF16 x
+        return V * H + 4 * V + io + R * 2 * H + 2 * R * (H + 4)
     if name == "nvfp4":
         return V * H // 2 + V * H // 16 + io
     if name == "q6k":
@@ -170,11 +191,13 @@ def cpu_baseline(name: str, cfg, rows: list[int], target_s: float):
     import synth
 
     x = synth.activations_bf16(cfg.index, max(max(rows), 1), max_rows=max(max(rows), 1))
+    if name == "w8a8_silu":
+        gate, up = synth.gate_up_bf16(cfg.index, max(rows), max_rows=max(rows))
 
     def run(n: int) -> float:
         wf = synth.weight_rows_f32(cfg.index, 0, n)
         vidx = np.arange(n, dtype=np.int64)
-        if name in ("fp8", "w8a8"):
+        if name in ("fp8", "w8a8", "w8a8_silu"):
             w, s = oracle.prep_fp8_rows(wf)
         elif name == "q6k":
             blocks = oracle.prep_q6k_rows(wf)
@@ -187,6 +210,9 @@ def cpu_baseline(name: str, cfg, rows: list[int], target_s: float):
                 oracle.fp8_rowscale_ref(w, s, x[:R], vidx)
             elif name == "w8a8":
                 xq, sa = oracle.quant_act_e4m3(x[:R])
+                oracle.w8a8_ref(w, s, xq, sa, vidx)
+            elif name == "w8a8_silu":
+                xq, sa, _ = oracle.quant_act_silu_e4m3(gate[:R], up[:R])
                 oracle.w8a8_ref(w, s, xq, sa, vidx)
             elif name == "nvfp4":
                 oracle.nvfp4_ref(wp, bs, g, x[:R], vidx)
@@ -252,12 +278,17 @@ def main():
     nx = max(max(rows), 1)
     xall = synth.activations_bf16(cfg.index, nx, max_rows=nx)
     xs = {R: torch.from_numpy(xall[:R].view(np.int16)).to(dev).view(torch.bfloat16) for R in rows}
+    if name == "w8a8_silu":
+        g_all, u_all = synth.gate_up_bf16(cfg.index, nx, max_rows=nx)
+        gd = torch.from_numpy(g_all.view(np.int16)).to(dev).view(torch.bfloat16)
+        ud = torch.from_numpy(u_all.view(np.int16)).to(dev).view(torch.bfloat16)
+    ncall = [0]
     if name == "dequant":
         outs = {0: torch.empty((V, H), dtype=torch.bfloat16, device=dev)}
     else:
         outs = {R: torch.empty((R, V), dtype=torch.bfloat16, device=dev) for R in rows}
     ws = None
-    if name == "w8a8":
+    if name in ("w8a8", "w8a8_silu"):
         ws = qh.w8a8_workspace(H, dev)
     elif name == "q6k":
         ws = torch.empty((qh.q6k_workspace_bytes(H),), dtype=torch.uint8, device=dev)
@@ -267,6 +298,10 @@ def main():
             qh.fp8_rowscale(head["codes"], head["scales"], xs[R], out=outs[R])
         elif name == "w8a8":
             qh.w8a8(head["codes"], head["scales"], xs[R], out=outs[R], workspace=ws)
+        elif name == "w8a8_silu":
+            w, sc = head["copies"][ncall[0] % SILU_WEIGHT_COPIES]
+            ncall[0] += 1
+            qh.w8a8_silu(w, sc, gd[:R], ud[:R], out=outs[R], workspace=ws)
         elif name == "nvfp4":
             qh.nvfp4(head["wp"], head["bs"], xs[R], head["g"], out=outs[R])
         elif name == "q6k":

@@ -142,6 +142,38 @@ int qhead_w8a8(const uint8_t* w_e4m3, const float* row_scale, const uint16_t* x_
                int32_t rows, int32_t hidden, int32_t vocab, uint16_t* out_bf16, void* workspace,
                size_t workspace_bytes, void* stream);
 
+/* The SiLU FFN product on its own ("w8a8_layer.rs", W8a8Ctx::silu_proj:
+ * bf16(silu(gate) * up)): out[i] = bf16( (g / (1 + exp(-g))) * u ) with
+ * g = gate[i], u = up[i], silu and product in binary64, one BF16 rounding
+ * (nearest even) -- the value qhead_quant_act_silu_e4m3 quantizes. gate, up,
+ * out: n BF16 values, 2-byte aligned. Finite inputs are assumed. */
+int qhead_silu_mul_bf16(const uint16_t* gate, const uint16_t* up, int64_t n, uint16_t* out_bf16,
+                        void* stream);
+
+/* Per-row E4M3 quantization of the SiLU FFN product, the down projection's
+ * activation ("w8a8_layer.rs", W8a8Ctx::silu_proj: bf16(silu(gate) * up)
+ * quantized in the launch that forms it):
+ *   p[r][k] = bf16( (g / (1 + exp(-g))) * u ), g = gate[r*ld + k],
+ *             u = up[r*ld + k], silu and product in binary64, one BF16
+ *             rounding (nearest even);
+ *   then xscale[r] and xq[r][k] from p exactly as qhead_quant_act_e4m3.
+ *  gate, up: [rows][ld] BF16, 16-byte aligned, ld >= hidden, ld % 8 == 0;
+ *  columns k >= hidden are not read. xq [rows][hidden], 8-byte aligned;
+ *  xscale [rows]. hidden must be a multiple of 16. Finite products are
+ *  assumed (an infinite p gives an unspecified row). */
+int qhead_quant_act_silu_e4m3(const uint16_t* gate, const uint16_t* up, int32_t ld,
+                              int32_t rows, int32_t hidden, uint8_t* xq, float* xscale,
+                              void* stream);
+
+/* W8A8 down projection of a SiLU FFN ("w8a8_layer.rs", W8a8Ctx::silu_proj):
+ * qhead_quant_act_silu_e4m3 into `workspace`, then qhead_w8a8_gemv, in
+ * chunks of <= 128 rows. The weight is [vocab][hidden] here with vocab = the
+ * projection's output width and hidden = the FFN width; other arguments as
+ * qhead_w8a8 and qhead_quant_act_silu_e4m3. */
+int qhead_w8a8_silu(const uint8_t* w_e4m3, const float* row_scale, const uint16_t* gate,
+                    const uint16_t* up, int32_t ld, int32_t rows, int32_t hidden, int32_t vocab,
+                    uint16_t* out_bf16, void* workspace, size_t workspace_bytes, void* stream);
+
 /* NVFP4 W4A16 head ("fp8_lut.rs" dequant_nvfp4_to_bf16 for the value
  * formula; "w4a16_gemv_tiers.rs" for the <= 8-row tiers):
  *   out[r][v] = bf16( fl32( global_scale * sum_b fl32(e4m3(bs[v][b]) * p_b) ) ),

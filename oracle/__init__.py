@@ -95,6 +95,7 @@ def lib():
             "orc_silu_mul_bf16": (ctypes.c_uint16, [ctypes.c_uint16, ctypes.c_uint16]),
             "orc_silu_mul_ambiguous": (ctypes.c_int, [ctypes.c_uint16, ctypes.c_uint16]),
             "orc_quant_act_silu_e4m3": (i64, [u16p, u16p, i32, i32, i32, u8p, f32p]),
+            "orc_silu_mul_bf16_array": (None, [u16p, u16p, i64, u16p, u8p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -185,6 +186,18 @@ def silu_mul_bf16(g_bits: int, u_bits: int) -> int:
 
 def silu_mul_ambiguous(g_bits: int, u_bits: int) -> bool:
     return bool(lib().orc_silu_mul_ambiguous(int(g_bits) & 0xFFFF, int(u_bits) & 0xFFFF))
+
+
+def silu_mul_bf16_array(g_bits: np.ndarray, u_bits: np.ndarray):
+    """Elementwise bf16(silu(g) * u) bits and ambiguity flags (same shape)."""
+    g = np.ascontiguousarray(g_bits, dtype=np.uint16)
+    u = np.ascontiguousarray(u_bits, dtype=np.uint16)
+    assert g.shape == u.shape
+    out = np.empty(g.shape, dtype=np.uint16)
+    amb = np.empty(g.shape, dtype=np.uint8)
+    lib().orc_silu_mul_bf16_array(_ptr(g, ctypes.c_uint16), _ptr(u, ctypes.c_uint16), g.size,
+                                  _ptr(out, ctypes.c_uint16), _ptr(amb, ctypes.c_uint8))
+    return out, amb.astype(bool)
 
 
 def quant_act_silu_e4m3(gate_bf16: np.ndarray, up_bf16: np.ndarray, hidden: int | None = None):

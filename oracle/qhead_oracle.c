@@ -241,6 +241,16 @@ ORC_API int orc_silu_mul_ambiguous(uint16_t g_bits, uint16_t u_bits) {
     return orc_bf16_rne(p * (1.0 - eps)) != b || orc_bf16_rne(p * (1.0 + eps)) != b;
 }
 
+/* Elementwise orc_silu_mul_bf16 with its ambiguity flag, over n values. */
+ORC_API void orc_silu_mul_bf16_array(const uint16_t* g, const uint16_t* u, int64_t n,
+                                     uint16_t* out, uint8_t* ambiguous) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) {
+        out[i] = orc_silu_mul_bf16(g[i], u[i]);
+        ambiguous[i] = (uint8_t)orc_silu_mul_ambiguous(g[i], u[i]);
+    }
+}
+
 /* Per-row E4M3 quantization of the SiLU product: p[r][k] =
  * orc_silu_mul_bf16(gate[r*ld + k], up[r*ld + k]) for k < hidden, then the
  * activation quantization above on p. Returns the number of ambiguous

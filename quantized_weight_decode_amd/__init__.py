@@ -61,6 +61,10 @@ _SIGS = {
     "qhead_q6k_gemv": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "qhead_q6k": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "qhead_quantize_fp8_rows": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
+    "qhead_silu_mul_bf16": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, _vp, _vp]),
+    "qhead_quant_act_silu_e4m3": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "qhead_w8a8_silu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
+                                       ctypes.c_size_t, _vp]),
     "qhead_quantize_nvfp4_rows": (ctypes.c_int, [_vp, _i32, _i32, _f32, _vp, _vp, _vp]),
     "qhead_quantize_q6k_rows": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
     "qhead_dequant_nvfp4_bf16": (ctypes.c_int, [_vp, _vp, _i32, _i32, _f32, _vp, _vp]),
@@ -199,6 +203,56 @@ def w8a8(w, row_scale, x, out=None, workspace=None, stream=None) -> torch.Tensor
                          _dev(x, "x", _BF16), rows, hidden, vocab, _dev(out, "out", _BF16),
                          _dev(workspace, "workspace", _U8), workspace.numel(), _stream(stream))
     _check(st, "qhead_w8a8")
+    return out
+
+
+def _silu_shapes(gate, up, hidden):
+    if gate.shape != up.shape or gate.dim() != 2:
+        raise ValueError("gate and up must be [rows, ld] tensors of one shape")
+    rows, ld = gate.shape
+    return rows, ld, ld if hidden is None else int(hidden)
+
+
+def silu_mul_bf16(gate, up, out=None, stream=None) -> torch.Tensor:
+    """bf16(silu(gate) * up) elementwise (silu and product in binary64)."""
+    if gate.shape != up.shape:
+        raise ValueError("gate and up must have one shape")
+    if out is None:
+        out = torch.empty(gate.shape, dtype=torch.bfloat16, device=gate.device)
+    st = _lib.qhead_silu_mul_bf16(_dev(gate, "gate", _BF16), _dev(up, "up", _BF16), gate.numel(),
+                                  _dev(out, "out", _BF16), _stream(stream))
+    _check(st, "qhead_silu_mul_bf16")
+    return out
+
+
+def quant_act_silu_e4m3(gate, up, hidden=None, xq=None, xscale=None, stream=None):
+    """Per-row E4M3 quantization of bf16(silu(gate) * up) over the first
+    `hidden` columns: (xq uint8 [rows, hidden], xscale f32 [rows])."""
+    rows, ld, hidden = _silu_shapes(gate, up, hidden)
+    if xq is None:
+        xq = torch.empty((rows, hidden), dtype=torch.uint8, device=gate.device)
+    if xscale is None:
+        xscale = torch.empty((rows,), dtype=torch.float32, device=gate.device)
+    st = _lib.qhead_quant_act_silu_e4m3(_dev(gate, "gate", _BF16), _dev(up, "up", _BF16), ld,
+                                        rows, hidden, _dev(xq, "xq", _U8),
+                                        _dev(xscale, "xscale", _F32), _stream(stream))
+    _check(st, "qhead_quant_act_silu_e4m3")
+    return xq, xscale
+
+
+def w8a8_silu(w, row_scale, gate, up, out=None, workspace=None, stream=None) -> torch.Tensor:
+    """W8A8 down projection of bf16(silu(gate) * up): w [n_out, k] E4M3 with
+    per-row scales, gate/up [rows, ld] BF16 (ld >= k); out [rows, n_out]."""
+    vocab, hidden = w.shape
+    rows, ld, _ = _silu_shapes(gate, up, hidden)
+    out = _out(out, rows, vocab, w.device)
+    if workspace is None:
+        workspace = w8a8_workspace(hidden, w.device)
+    st = _lib.qhead_w8a8_silu(_dev(w, "w", _U8), _dev(row_scale, "row_scale", _F32),
+                              _dev(gate, "gate", _BF16), _dev(up, "up", _BF16), ld, rows, hidden,
+                              vocab, _dev(out, "out", _BF16), _dev(workspace, "workspace", _U8),
+                              workspace.numel(), _stream(stream))
+    _check(st, "qhead_w8a8_silu")
     return out
 
 

@@ -216,6 +216,66 @@ int qhead_w8a8(const uint8_t* w_e4m3, const float* row_scale, const uint16_t* x_
     return QHEAD_OK;
 }
 
+int qhead_silu_mul_bf16(const uint16_t* gate, const uint16_t* up, int64_t n, uint16_t* out_bf16,
+                        void* stream) {
+    if (n < 0) return QHEAD_ERR_SHAPE;
+    if (n == 0) return QHEAD_OK;
+    if (!gate || !up || !out_bf16) return QHEAD_ERR_NULL;
+    if (!aligned(gate, 2) || !aligned(up, 2) || !aligned(out_bf16, 2)) return QHEAD_ERR_ALIGN;
+    DeviceInfo dev;
+    if (int st = device_or_error(&dev)) return st;
+    return hip_status(run_silu_mul(gate, up, n, out_bf16, dev, static_cast<hipStream_t>(stream)));
+}
+
+int qhead_quant_act_silu_e4m3(const uint16_t* gate, const uint16_t* up, int32_t ld,
+                              int32_t rows, int32_t hidden, uint8_t* xq, float* xscale,
+                              void* stream) {
+    if (rows < 0 || hidden <= 0 || hidden % 16 || ld < hidden || ld % 8) return QHEAD_ERR_SHAPE;
+    if (rows == 0) return QHEAD_OK;
+    if (!gate || !up || !xq || !xscale) return QHEAD_ERR_NULL;
+    if (!aligned(gate, 16) || !aligned(up, 16) || !aligned(xq, 8) || !aligned(xscale, 4))
+        return QHEAD_ERR_ALIGN;
+    DeviceInfo dev;
+    if (int st = device_or_error(&dev)) return st;
+    return hip_status(run_quant_act_silu_e4m3(gate, up, ld, rows, hidden, xq, xscale,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int qhead_w8a8_silu(const uint8_t* w_e4m3, const float* row_scale, const uint16_t* gate,
+                    const uint16_t* up, int32_t ld, int32_t rows, int32_t hidden, int32_t vocab,
+                    uint16_t* out_bf16, void* workspace, size_t workspace_bytes, void* stream) {
+    if (rows < 0 || hidden <= 0 || vocab <= 0 || hidden % 16 || ld < hidden || ld % 8)
+        return QHEAD_ERR_SHAPE;
+    if (rows == 0) return QHEAD_OK;
+    if (!w_e4m3 || !row_scale || !gate || !up || !out_bf16) return QHEAD_ERR_NULL;
+    if (!aligned(w_e4m3, 16) || !aligned(gate, 16) || !aligned(up, 16) ||
+        !aligned(row_scale, 4) || !aligned(out_bf16, 2))
+        return QHEAD_ERR_ALIGN;
+    if (!workspace || workspace_bytes < qhead_w8a8_workspace_bytes(hidden))
+        return QHEAD_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return QHEAD_ERR_ALIGN;
+    DeviceInfo dev;
+    if (int st = device_or_error(&dev)) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* xq = static_cast<uint8_t*>(workspace);
+    float* sa = reinterpret_cast<float*>(xq + align256((size_t)128 * hidden));
+    for (int32_t done = 0; done < rows;) {
+        const int32_t m = (rows - done) < 128 ? (rows - done) : 128;
+        const size_t off = (size_t)done * ld;
+        hipError_t e = run_quant_act_silu_e4m3(gate + off, up + off, ld, m, hidden, xq, sa, s);
+        if (e != hipSuccess) return QHEAD_ERR_HIP;
+        for (int32_t g = 0; g < m;) {
+            const int32_t gm = (m - g) < kW8A8GemvRows ? (m - g) : kW8A8GemvRows;
+            e = run_fp8_w8a8(w_e4m3, row_scale, xq + (size_t)g * hidden, sa + g, gm, hidden, vocab,
+                             out_bf16 + (size_t)(done + g) * vocab, dev, s);
+            if (e != hipSuccess) return QHEAD_ERR_HIP;
+            g += gm;
+        }
+        done += m;
+    }
+    return QHEAD_OK;
+}
+
 int qhead_nvfp4(const uint8_t* w_packed, const uint8_t* block_scale, const uint16_t* x_bf16,
                 int32_t rows, int32_t hidden, int32_t vocab, uint16_t* out_bf16,
                 float global_scale, void* stream) {

@@ -12,95 +12,89 @@
 //    dequant_nvfp4_e8m0_to_bf16 and FP8_E8M0_LUT: 2^(e-127), e = 0 and
 //    e = 255 give 0): out = bf16( fl32(e2m1 * scale) ).
 //
-// Both are HBM streams (0.5625 bytes in, 2 bytes out per value). Each thread
-// converts 32 (NVFP4) or 16 (E8M0) consecutive values: one coalesced packed
-// load, exact v_cvt_scalef32_pk_f32_fp4 conversions, and 16-byte streaming
-// stores of the BF16 results.
+// Both are HBM streams (0.5625 bytes in, 2 bytes out per value). A lane
+// converts one group of 8 consecutive values at a time: a 4-byte packed load
+// and a 1-byte scale load, exact v_cvt_scalef32_pk_f32_fp4 conversions, the
+// scale products in binary32, v_cvt_pk_bf16_f32 (nearest even) and one
+// 16-byte streaming store. Consecutive lanes take consecutive groups, so
+// every load and store instruction of a wave covers one contiguous span; a
+// workgroup handles kUnroll * 256 groups per iteration with all loads issued
+// before the first conversion.
 #include "qhead_device.h"
 #include "qhead_internal.h"
 
 namespace qh {
 
 constexpr int kDqThreads = 256;
+constexpr int kUnroll = 4;
 
-// Four F32 pairs from the four bytes of w (each byte: low nibble first).
-__device__ __forceinline__ void e2m1x8_to_f32(uint32_t w, float (&f)[8]) {
-    const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-    const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-    const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-    const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-    f[0] = p0[0]; f[1] = p0[1]; f[2] = p1[0]; f[3] = p1[1];
-    f[4] = p2[0]; f[5] = p2[1]; f[6] = p3[0]; f[7] = p3[1];
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
-}
-
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4s_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void store_stream16(uint16_t* p, uint32_t a, uint32_t b, uint32_t c,
-                                               uint32_t d) {
-    u32x4s_t v = {a, b, c, d};
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4s_t*>(p));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// Values 2Q and 2Q+1 of a group (byte Q of w, low nibble first) times s,
+// then times g if kGlobal, packed to BF16.
+template <int Q, bool kGlobal>
+__device__ __forceinline__ uint32_t convert2(uint32_t w, float s, float g) {
+    const auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, Q);
+    float a = p[0] * s, b = p[1] * s;
+    if (kGlobal) {
+        a = a * g;
+        b = b * g;
+    }
+    return pack_bf16x2(a, b);
+}
+
+template <bool kGlobal>
+__device__ __forceinline__ u32x4s_t convert8(uint32_t w, float s, float g) {
+    u32x4s_t o;
+    o[0] = convert2<0, kGlobal>(w, s, g);
+    o[1] = convert2<1, kGlobal>(w, s, g);
+    o[2] = convert2<2, kGlobal>(w, s, g);
+    o[3] = convert2<3, kGlobal>(w, s, g);
+    return o;
+}
+
+// groups = total / 8; the scale of group i is scale_f32(sc[i / per_scale]).
+template <bool kE8M0>
 __global__ void __launch_bounds__(kDqThreads)
-dequant_nvfp4_bf16_kernel(const uint8_t* __restrict__ wp, const uint8_t* __restrict__ bs, float g,
-                          int64_t n, int k, uint16_t* __restrict__ out) {
-    const int64_t per_row = k / 32;
-    const int64_t chunks = n * per_row;
-    const int64_t stride = (int64_t)gridDim.x * kDqThreads;
-    for (int64_t c = (int64_t)blockIdx.x * kDqThreads + threadIdx.x; c < chunks; c += stride) {
-        const int64_t v = c / per_row;
-        const int j = (int)(c - v * per_row);
-        const int64_t flat0 = v * k + 32 * (int64_t)j;
-        const uint4 p = load_stream16(wp + flat0 / 2);
-        const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(bs + v * (k / 16) + 2 * j);
-        const float s[2] = {__builtin_amdgcn_cvt_f32_fp8(sc2, 0),
-                            __builtin_amdgcn_cvt_f32_fp8(sc2, 1)};
-        const uint32_t d[4] = {p.x, p.y, p.z, p.w};
-        uint32_t o[16];
+dequant_fp4_kernel(const uint32_t* __restrict__ wp, const uint8_t* __restrict__ sc, float g,
+                   int64_t groups, int64_t per_scale, uint16_t* __restrict__ out) {
+    const int64_t tile = (int64_t)kUnroll * kDqThreads;
+    for (int64_t base = (int64_t)blockIdx.x * tile; base < groups;
+         base += (int64_t)gridDim.x * tile) {
+        uint32_t w[kUnroll];
+        uint32_t e[kUnroll];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            float f[8];
-            e2m1x8_to_f32(d[q], f);
-            const float sq = s[q >> 1];  // dwords 0,1 hold block 0; 2,3 block 1
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                o[4 * q + i] = pack_bf16x2((f[2 * i] * sq) * g, (f[2 * i + 1] * sq) * g);
+        for (int u = 0; u < kUnroll; ++u) {
+            int64_t i = base + u * kDqThreads + threadIdx.x;
+            i = i < groups ? i : groups - 1;  // clamped: the store below is guarded
+            w[u] = wp[i];
+            e[u] = sc[i / per_scale];
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            store_stream16(out + flat0 + 8 * q, o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t i = base + u * kDqThreads + threadIdx.x;
+            float s;
+            if (kE8M0)
+                s = (e[u] == 0u || e[u] == 255u) ? 0.0f : __uint_as_float(e[u] << 23);
+            else
+                s = __builtin_amdgcn_cvt_f32_fp8(e[u], 0);
+            const u32x4s_t o = convert8<!kE8M0>(w[u], s, g);
+            if (i < groups)
+                __builtin_nontemporal_store(o, reinterpret_cast<u32x4s_t*>(out + 8 * i));
+        }
     }
 }
 
-__global__ void __launch_bounds__(kDqThreads)
-dequant_fp4_e8m0_bf16_kernel(const uint8_t* __restrict__ wp, const uint8_t* __restrict__ scales,
-                             int64_t total, int64_t block, uint16_t* __restrict__ out) {
-    const int64_t chunks = total / 16;
-    const int64_t stride = (int64_t)gridDim.x * kDqThreads;
-    for (int64_t c = (int64_t)blockIdx.x * kDqThreads + threadIdx.x; c < chunks; c += stride) {
-        const int64_t flat0 = 16 * c;
-        const uint2 p = *reinterpret_cast<const uint2*>(wp + flat0 / 2);
-        const uint32_t e = scales[flat0 / block];
-        const float sc = (e == 0u || e == 255u) ? 0.0f : __uint_as_float(e << 23);
-        uint32_t o[8];
-        float f[8];
-        e2m1x8_to_f32(p.x, f);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(f[2 * i] * sc, f[2 * i + 1] * sc);
-        e2m1x8_to_f32(p.y, f);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[4 + i] = pack_bf16x2(f[2 * i] * sc, f[2 * i + 1] * sc);
-        store_stream16(out + flat0, o[0], o[1], o[2], o[3]);
-        store_stream16(out + flat0 + 8, o[4], o[5], o[6], o[7]);
-    }
-}
-
-static unsigned grid_for(int64_t chunks, const DeviceInfo& dev) {
-    int64_t blocks = (chunks + kDqThreads - 1) / kDqThreads;
+static unsigned grid_for(int64_t groups, const DeviceInfo& dev) {
+    const int64_t tile = (int64_t)kUnroll * kDqThreads;
+    int64_t blocks = (groups + tile - 1) / tile;
     const int64_t cap = (int64_t)dev.num_cus * 8;
     if (blocks > cap) blocks = cap;
     return (unsigned)(blocks > 0 ? blocks : 1);
@@ -108,16 +102,20 @@ static unsigned grid_for(int64_t chunks, const DeviceInfo& dev) {
 
 hipError_t run_dequant_nvfp4_bf16(const uint8_t* wp, const uint8_t* bs, float g, int64_t n, int k,
                                   uint16_t* out, const DeviceInfo& dev, hipStream_t stream) {
-    hipLaunchKernelGGL(dequant_nvfp4_bf16_kernel, dim3(grid_for(n * (k / 32), dev)),
-                       dim3(kDqThreads), 0, stream, wp, bs, g, n, k, out);
+    const int64_t groups = n * (int64_t)k / 8;  // k % 32 == 0: a group never spans rows
+    hipLaunchKernelGGL(dequant_fp4_kernel<false>, dim3(grid_for(groups, dev)), dim3(kDqThreads),
+                       0, stream, reinterpret_cast<const uint32_t*>(wp), bs, g, groups,
+                       (int64_t)2, out);
     return hipGetLastError();
 }
 
 hipError_t run_dequant_fp4_e8m0_bf16(const uint8_t* wp, const uint8_t* scales, int64_t total,
                                      int64_t block, uint16_t* out, const DeviceInfo& dev,
                                      hipStream_t stream) {
-    hipLaunchKernelGGL(dequant_fp4_e8m0_bf16_kernel, dim3(grid_for(total / 16, dev)),
-                       dim3(kDqThreads), 0, stream, wp, scales, total, block, out);
+    const int64_t groups = total / 8;  // block % 16 == 0: a group never spans scale groups
+    hipLaunchKernelGGL(dequant_fp4_kernel<true>, dim3(grid_for(groups, dev)), dim3(kDqThreads),
+                       0, stream, reinterpret_cast<const uint32_t*>(wp), scales, 0.0f, groups,
+                       block / 8, out);
     return hipGetLastError();
 }
 

@@ -269,9 +269,9 @@ hipError_t run_nvfp4(const uint8_t* Wp, const uint8_t* bs, const uint16_t* x, fl
     case RR:                            \
         return launch_nvfp4<RR, TT, WV, MB, BPC>(Wp, bs, x, g, H, V, out, dev, stream);
         QH_F4_CASE(1, 2, 16, 20, 1)
-        QH_F4_CASE(2, 2, 16, 20, 1)
-        QH_F4_CASE(3, 2, 16, 20, 1)
-        QH_F4_CASE(4, 2, 16, 20, 1)
+        QH_F4_CASE(2, 4, 8, 8, 2)
+        QH_F4_CASE(3, 2, 8, 12, 2)
+        QH_F4_CASE(4, 2, 8, 12, 2)
         QH_F4_CASE(5, 4, 8, 12, 1)
         QH_F4_CASE(6, 4, 8, 12, 1)
         QH_F4_CASE(7, 4, 8, 12, 1)

@@ -17,15 +17,15 @@
 // Mapping (MI355X-first): 16 lanes per super-block, lane t of the 16 owns
 // sub-block t = the 16 consecutive weights 16t .. 16t+15, whose low bits are
 // 16 consecutive ql bytes and whose high bits are 16 consecutive qh bytes. A
-// wave covers four super-blocks (1024 weights) per segment. Super-blocks are
-// only 2-byte aligned (210 bytes), so each 16-byte field is read as five
-// aligned dwords and realigned with v_alignbyte (the extra dword stays
-// inside the super-block). The -32 offset is folded into the integer dot:
-// the staging step stores -32 * sum(q8) per sub-block next to the q8 values.
-// Weight loads are ordinary (cached) loads, not streaming ones: the ql, qh,
-// scale and d fields of one super-block share 128-byte lines across several
-// load instructions, and streaming loads re-fetched those lines (about 8 %
-// more HBM bytes and 25 % more time, measured).
+// wave covers four super-blocks (1024 weights, 840 bytes) of each of its T
+// vocab rows per item. Those 840 bytes are fetched with one fully coalesced
+// 16-byte load per lane (the aligned 16-byte chunks that hold them; a chunk
+// holding at least one byte of the item never crosses a page) and written
+// to a wave-private LDS buffer; each lane then reads its fields from LDS as
+// aligned dwords and realigns them with v_alignbyte (super-blocks are only
+// 2-byte aligned). Two items are in flight in registers while one is being
+// computed from LDS. The -32 offset is folded into the integer dot: the
+// staging step stores -32 * sum(q8) per sub-block next to the q8 values.
 #include "qhead_device.h"
 #include "qhead_internal.h"
 
@@ -78,8 +78,12 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     constexpr int N = T * R;
     constexpr int NP = next_pow2(N);
     constexpr int M = Log2<NP>::value;
+    constexpr int kItemBytes = 4 * kQ6KBlockBytes;  // 840
     static_assert(NP <= 64 && R <= 8, "T*R must be <= 64, R <= 8");
+    static_assert(kItemBytes + 15 <= 64 * 16, "an item must fit one 16-byte load per lane");
     __shared__ Q6Lds<R> L;
+    // wave-private weight staging: [wave][buffer][row t][1024 bytes]
+    __shared__ u32x4_t WB[WAVES][2][T][kWave];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -89,8 +93,9 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     const int NT = (H + kQTileK - 1) / kQTileK;
     const int nsb = H / 256;
     const size_t rowbytes = (size_t)nsb * kQ6KBlockBytes;
+    const uintptr_t base_addr = reinterpret_cast<uintptr_t>(blocks);
 
-    // lane -> (super-block within the segment, sub-block t = 8n + 2c + h)
+    // lane -> (super-block within the item, sub-block t = 8n + 2c + h)
     const int sbi = lane >> 4;
     const int t16 = lane & 15;
     const int n = t16 >> 3, c = (t16 >> 1) & 3, h = t16 & 1;
@@ -103,18 +108,6 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     const int my_r = my_idx / T;
     const int my_t = my_idx - my_r * T;
     const bool writer = ((lane & ((1 << (6 - M)) - 1)) == 0) && (my_idx < N);
-
-    // Raw bytes of one item: for each of T rows, the lane's 16 ql and 16 qh
-    // bytes as five aligned dwords each (a 210-byte super-block is only
-    // 2-byte aligned; the fifth dword stays inside the super-block), its
-    // int8 scale and the fp16 d.
-    struct Item {
-        uint32_t ql[T][5];
-        uint32_t qh[T][5];
-        uint32_t sc[T];
-        uint32_t d[T];
-        uint32_t sh[T];
-    };
 
     for (int sj = 0; sj < nsuper; ++sj) {
         float part[MAXB];
@@ -134,37 +127,44 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
             const int first = (sj * MAXB) * TW + gw;
             const int nbb = first < NB ? min(MAXB, (NB - 1 - first) / TW + 1) : 0;
             const int nitems = nbb * nseg;
-            // Unconditional loads: lanes past the last super-block of the
-            // row re-read the last one and rows past the vocab tail re-read
-            // the last row; their contributions are zeroed or never stored.
-            auto load_item = [&](int bi, int s, Item& dst) {
-                const int v0 = ((sj * MAXB + bi) * TW + gw) * T;
-                const int sb = min(tt * kQSbPerTile + s * 4 + sbi, nsb - 1);
+
+            // Absolute address of the first byte of item (bi, s) in row t;
+            // rows past the vocab tail re-read the last row (never stored).
+            auto item_addr = [&](int bi, int s, int t) -> uintptr_t {
+                const int v = min(((sj * MAXB + bi) * TW + gw) * T + t, V - 1);
+                const int sb0 = tt * kQSbPerTile + s * 4;
+                return base_addr + (size_t)v * rowbytes + (size_t)sb0 * kQ6KBlockBytes;
+            };
+            // One 16-byte aligned chunk per lane; lanes past the item's last
+            // chunk re-read it.
+            auto issue = [&](int bi, int s, u32x4_t (&g)[T]) {
+                const int sb0 = tt * kQSbPerTile + s * 4;
+                const int nbytes = min(4, nsb - sb0) * kQ6KBlockBytes;
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
-                    const int v = min(v0 + t, V - 1);
-                    const uint8_t* blk = blocks + (size_t)v * rowbytes + (size_t)sb * kQ6KBlockBytes;
-                    const uintptr_t a = reinterpret_cast<uintptr_t>(blk);
-                    const uint32_t* base = reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3);
-                    dst.sh[t] = (uint32_t)(a & 3);
-#pragma unroll
-                    for (int i = 0; i < 5; ++i) {
-                        dst.ql[t][i] = base[ql_off / 4 + i];
-                        dst.qh[t][i] = base[qh_off / 4 + i];
-                    }
-                    dst.sc[t] = blk[192 + t16];
-                    dst.d[t] = *reinterpret_cast<const uint16_t*>(blk + 208);
+                    const uintptr_t a = item_addr(bi, s, t);
+                    const uintptr_t a16 = a & ~(uintptr_t)15;
+                    const int last = (int)(((a + nbytes - 1) & ~(uintptr_t)15) - a16) >> 4;
+                    const int ch = min(lane, last);
+                    g[t] = *reinterpret_cast<const u32x4_t*>(a16 + 16 * (uintptr_t)ch);
                 }
             };
+            auto stage = [&](int buf, const u32x4_t (&g)[T]) {
+#pragma unroll
+                for (int t = 0; t < T; ++t) WB[wave][buf][t][lane] = g[t];
+            };
+
             float acc[NP];
             int bi = 0, s = 0;
-            auto step = [&](int it, const Item& cur, Item& nxt) {
-                {
-                    const bool last = it + 1 >= nitems;
-                    const int nbi = last ? bi : ((s + 1 == nseg) ? bi + 1 : bi);
-                    const int ns = last ? s : ((s + 1 == nseg) ? 0 : s + 1);
-                    load_item(nbi, ns, nxt);
-                }
+            // Item `it` is in LDS buffer `buf`; item it + 1 is in flight in
+            // `gn`; `gf` is free and receives item it + 2.
+            auto step = [&](int it, int buf, u32x4_t (&gf)[T], const u32x4_t (&gn)[T]) {
+                // (bi, s) of items it + 1 and it + 2, clamped to the last item
+                int bi1 = bi, s1 = s;
+                if (it + 1 < nitems) { if (++s1 == nseg) { s1 = 0; ++bi1; } }
+                int bi2 = bi1, s2 = s1;
+                if (it + 2 < nitems) { if (++s2 == nseg) { s2 = 0; ++bi2; } }
+                issue(bi2, s2, gf);
                 if (s == 0) {
 #pragma unroll
                     for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
@@ -175,18 +175,29 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                 float wsc[T];
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
+                    const uintptr_t a = item_addr(bi, s, t);
+                    const int rel = (int)(a & 15) + sbi * kQ6KBlockBytes;  // LDS byte offset
+                    const uint32_t sh = (uint32_t)(rel & 3);
+                    const uint8_t* lb = reinterpret_cast<const uint8_t*>(&WB[wave][buf][t][0]);
+                    const uint32_t* lw = reinterpret_cast<const uint32_t*>(lb + (rel & ~3));
+                    uint32_t qlw[5], qhw[5];
+#pragma unroll
+                    for (int i = 0; i < 5; ++i) {
+                        qlw[i] = lw[ql_off / 4 + i];
+                        qhw[i] = lw[qh_off / 4 + i];
+                    }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const uint32_t ql =
-                            __builtin_amdgcn_alignbyte(cur.ql[t][i + 1], cur.ql[t][i], cur.sh[t]);
-                        const uint32_t qh =
-                            __builtin_amdgcn_alignbyte(cur.qh[t][i + 1], cur.qh[t][i], cur.sh[t]);
+                        const uint32_t ql = __builtin_amdgcn_alignbyte(qlw[i + 1], qlw[i], sh);
+                        const uint32_t qh = __builtin_amdgcn_alignbyte(qhw[i + 1], qhw[i], sh);
                         qw[t][i] = ((ql >> lo_shift) & 0x0F0F0F0Fu) |
                                    (((qh >> hi_shift) & 0x03030303u) << 4);
                     }
+                    const int sc = (int)(int8_t)lb[rel + 192 + t16];
+                    const uint16_t dbits = *reinterpret_cast<const uint16_t*>(lb + rel + 208);
                     // d * sc is exact in FP32 (11-bit times 8-bit significands)
-                    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)cur.d[t]);
-                    wsc[t] = valid ? d * (float)(int)(int8_t)cur.sc[t] : 0.0f;
+                    const float d = (float)__builtin_bit_cast(_Float16, dbits);
+                    wsc[t] = valid ? d * (float)sc : 0.0f;
                 }
                 const int kk = min(sbt, kQSbPerTile - 1) * 256 + 16 * t16;  // k within the tile
 #pragma unroll
@@ -203,6 +214,8 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                         acc[r * T + t] = __builtin_fmaf((float)is, wsc[t] * d8, acc[r * T + t]);
                     }
                 }
+                // item it + 1 into the other buffer (its last reader was item it - 1)
+                stage(buf ^ 1, gn);
                 if (s + 1 == nseg) {
                     wave_reduce_scatter<NP>(acc, lane);
 #pragma unroll
@@ -214,15 +227,19 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                     ++s;
                 }
             };
-            Item bufA, bufB;
-            if (nitems > 0) load_item(0, 0, bufA);
-            int it = 0;
-#pragma unroll 1
-            for (; it + 1 < nitems; it += 2) {
-                step(it, bufA, bufB);
-                step(it + 1, bufB, bufA);
+            u32x4_t gA[T], gB[T];
+            if (nitems > 0) {
+                issue(0, 0, gA);
+                stage(0, gA);
+                int bi1 = 0, s1 = 0;
+                if (nitems > 1) { if (++s1 == nseg) { s1 = 0; ++bi1; } }
+                issue(bi1, s1, gB);
             }
-            if (it < nitems) step(it, bufA, bufB);
+#pragma unroll 1
+            for (int it = 0; it < nitems; it += 2) {
+                step(it, 0, gA, gB);
+                if (it + 1 < nitems) step(it + 1, 1, gB, gA);
+            }
         }
 
 #pragma unroll
@@ -254,10 +271,10 @@ hipError_t run_q6k(const uint8_t* blocks, const uint8_t* q8, int R, int H, int V
 #define QH_Q6_CASE(RR, TT, WV, MB, BPC) \
     case RR:                            \
         return launch_q6k<RR, TT, WV, MB, BPC>(blocks, q8, H, V, out, dev, stream);
-        QH_Q6_CASE(1, 2, 16, 20, 1)
-        QH_Q6_CASE(2, 2, 16, 20, 1)
-        QH_Q6_CASE(3, 2, 16, 20, 1)
-        QH_Q6_CASE(4, 2, 16, 20, 1)
+        QH_Q6_CASE(1, 4, 8, 12, 2)
+        QH_Q6_CASE(2, 4, 8, 12, 1)
+        QH_Q6_CASE(3, 4, 8, 12, 1)
+        QH_Q6_CASE(4, 4, 8, 12, 1)
         QH_Q6_CASE(5, 4, 8, 12, 1)
         QH_Q6_CASE(6, 4, 8, 12, 1)
         QH_Q6_CASE(7, 4, 8, 12, 1)

@@ -25,6 +25,10 @@ hipError_t run_fp8_w8a8(const uint8_t* W, const float* sw, const uint8_t* xq, co
 // Activation quantizers and weight preparation.
 hipError_t run_quant_act_e4m3(const uint16_t* x, int rows, int H, uint8_t* xq, float* sa,
                               hipStream_t stream);
+hipError_t run_quant_act_silu_e4m3(const uint16_t* gate, const uint16_t* up, int ld, int rows,
+                                   int H, uint8_t* xq, float* sa, hipStream_t stream);
+hipError_t run_silu_mul(const uint16_t* gate, const uint16_t* up, int64_t n, uint16_t* out,
+                        const DeviceInfo& dev, hipStream_t stream);
 hipError_t run_quant_q8_1(const uint16_t* x, int rows, int H, uint8_t* q8, hipStream_t stream);
 hipError_t run_quantize_fp8_rows(const float* w, int V, int H, uint8_t* codes, float* scales,
                                  hipStream_t stream);

@@ -16,12 +16,16 @@ the NVFP4 head of "w4a16_gemv_tiers.rs" and the Q6_K head of "lm_head_q6k.rs"):
   cfg2  FP8 W8A16  vocab 155136 x hidden 8192, W ~ N(0, 0.015) (1.27 GB head)
   cfg3  W8A8       vocab 129280 x hidden 7168, W ~ N(0, 0.02)
   cfg4  NVFP4 / Q6_K vocab 129280 x hidden 7168, W ~ N(0, 0.02)
+  cfg5  W8A8 SiLU down projection: output 7168 x FFN width 18432,
+        W ~ N(0, 0.02); gate ~ N(0, 1.5^2), up ~ N(0, 1) (the FFN's
+        activation is bf16(silu(gate) * up), "w8a8_layer.rs" silu_proj)
 
 Weights are drawn in independent 1024-row chunks, chunk c of config i seeded
 with SeedSequence([100 + i, c]), so any vocab row range can be regenerated on
 its own. Activations for config i use seed 200 + i and are drawn once for the
 configuration's largest row count; a smaller row count takes the leading rows.
-The outlier channels of cfg1 are drawn with seed 300 + i.
+The outlier channels of cfg1 are drawn with seed 300 + i; the gate and up
+rows of cfg5 with seeds 400 + i and 500 + i.
 """
 
 from __future__ import annotations
@@ -57,6 +61,8 @@ CONFIGS = {
                   "w8a8 head 129280x7168"),
     4: HeadConfig(4, "nvfp4q6k", 129280, 7168, 0.02, (1, 2, 3, 4, 5, 6, 7, 8), 0,
                   "nvfp4 / q6_k head 129280x7168"),
+    5: HeadConfig(5, "w8a8silu", 7168, 18432, 0.02, (1, 16, 128, 130), 0,
+                  "w8a8 silu down projection 7168x18432"),
 }
 
 
@@ -143,6 +149,20 @@ def to_bf16_bits(a: np.ndarray) -> np.ndarray:
 
 def activations_bf16(cfg_index: int, rows: int, **kw) -> np.ndarray:
     return to_bf16_bits(activations_f32(cfg_index, rows, **kw))
+
+
+def gate_up_bf16(cfg_index: int, rows: int, *, hidden: int | None = None,
+                 max_rows: int | None = None):
+    """BF16 bits of the SiLU FFN's gate [rows, hidden] ~ N(0, 1.5^2) and up
+    [rows, hidden] ~ N(0, 1): the leading rows of one seeded draw each."""
+    cfg = CONFIGS.get(cfg_index)
+    hidden = hidden if hidden is not None else cfg.hidden
+    max_rows = max(max_rows if max_rows is not None else max(cfg.rows), rows)
+    gg = np.random.Generator(np.random.PCG64(400 + cfg_index))
+    gu = np.random.Generator(np.random.PCG64(500 + cfg_index))
+    gate = gg.standard_normal((max_rows, hidden), dtype=np.float32) * np.float32(1.5)
+    up = gu.standard_normal((max_rows, hidden), dtype=np.float32)
+    return to_bf16_bits(gate[:rows]), to_bf16_bits(up[:rows])
 
 
 def random_bytes(seed: int, n: int) -> np.ndarray:

@@ -42,11 +42,18 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+# Half the spacing of BF16's subnormals (2^-133): no BF16 value lies closer
+# than this to every real number in BF16's subnormal range, where 2^-7 |ref|
+# is smaller than the output format can resolve.
+BF16_SUBNORMAL_HALF_SPACING = 2.0 ** -134
+
+
 def assert_within_bound(got_bits: np.ndarray, ref: np.ndarray, absdot: np.ndarray, what: str):
-    """|gpu - ref| <= 2^-7 |ref| + 1e-4 sum|x w| for every logit."""
+    """|gpu - ref| <= 2^-7 |ref| + 1e-4 sum|x w| for every logit, read with a
+    floor of 2^-134 for logits in BF16's subnormal range."""
     got = bf16_bits_to_f64(got_bits)
     err = np.abs(got - ref)
-    bound = 2.0 ** -7 * np.abs(ref) + 1e-4 * absdot
+    bound = 2.0 ** -7 * np.abs(ref) + 1e-4 * absdot + BF16_SUBNORMAL_HALF_SPACING
     bad = ~(err <= bound)
     if bad.any():
         idx = np.argwhere(bad)[:5]

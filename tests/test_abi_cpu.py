@@ -31,7 +31,7 @@ MIS = 0x10001
 
 def test_exports_every_declared_function(qh):
     names = qh.header_functions()
-    assert len(names) == 18
+    assert len(names) == 21
     for n in names:
         assert hasattr(qh.lib(), n), n
     out = subprocess.run(["nm", "-D", "--defined-only", qh.LIB_PATH], capture_output=True,
@@ -136,6 +136,31 @@ def test_quantize_fp8_rows_validation(qh):
     assert f(A16, 8, 24, A16, A16, None) == -2
     assert f(A16 + 4, 8, 16, A16, A16, None) == -3
     assert f(A16, 0, 16, A16, A16, None) == 0
+
+
+def test_silu_validation(qh):
+    L = qh.lib()
+    m = L.qhead_silu_mul_bf16
+    assert m(A16, A16, -1, A16, None) == -2
+    assert m(A16, None, 8, A16, None) == -1
+    assert m(A16, A16, 8, MIS, None) == -3
+    assert m(None, None, 0, None, None) == 0
+    f = L.qhead_quant_act_silu_e4m3
+    assert f(A16, A16, 64, 2, 24, A16, A16, None) == -2     # hidden % 16
+    assert f(A16, A16, 48, 2, 64, A16, A16, None) == -2     # ld < hidden
+    assert f(A16, A16, 68, 2, 64, A16, A16, None) == -2     # ld % 8
+    assert f(A16, None, 64, 2, 64, A16, A16, None) == -1
+    assert f(A16, A16 + 8, 64, 2, 64, A16, A16, None) == -3
+    assert f(A16, A16, 64, 2, 64, A16 + 4, A16, None) == -3
+    assert f(None, None, 64, 0, 64, None, None, None) == 0   # rows = 0: no launch
+    ws = qh.w8a8_workspace_bytes(64)
+    g = L.qhead_w8a8_silu
+    assert g(A16, A16, A16, A16, 64, 1, 64, 8, A16, A256, ws - 1, None) == -4
+    assert g(A16, A16, A16, A16, 56, 1, 64, 8, A16, A256, ws, None) == -2
+    assert g(A16, A16, A16, None, 64, 1, 64, 8, A16, A256, ws, None) == -1
+    assert g(A16, A16, A16, A16 + 2, 64, 1, 64, 8, A16, A256, ws, None) == -3
+    assert g(A16, A16, A16, A16, 64, 1, 64, 8, A16, A256 + 64, ws, None) == -3
+    assert g(None, None, None, None, 64, 0, 64, 8, None, None, 0, None) == 0
 
 
 def test_quantize_nvfp4_q6k_rows_validation(qh):
