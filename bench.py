@@ -71,7 +71,8 @@ WORKLOADS = {
         "synthetic (seeded N(0,0.015) weights quantized per row to E4M3, N(0,1) BF16 x)"),
     "w8a8": Workload(
         3, "1,16,128", "fp8_gemv_kernel<W8A8> + quant_act_e4m3_kernel (per call)",
-        ("fp8_gemv.hip", "quant.hip", "qhead_device.h"), "w8a8_129280x7168_counters.json",
+        ("fp8_gemv.hip", "act_quant.hip", "quant_common.h", "qhead_device.h"),
+        "w8a8_129280x7168_counters.json",
         "achieved HBM GB/s, W8A8 head 129280x7168, calls of 1/16/128 rows",
         "fp8e4m3 x fp8e4m3 -> f32 acc, bf16 out", _W002),
     "nvfp4": Workload(
@@ -81,18 +82,20 @@ WORKLOADS = {
         "e2m1 x e4m3 block scale x bf16 -> f32 acc, bf16 out", _W002),
     "q6k": Workload(
         4, "1,2,4,8", "q6k_gemv_kernel + quant_q8_1_kernel (per call)",
-        ("q6k_gemv.hip", "quant.hip", "qhead_device.h"), "q6k_gemv_129280x7168_counters.json",
+        ("q6k_gemv.hip", "act_quant.hip", "quant_common.h", "qhead_device.h"),
+        "q6k_gemv_129280x7168_counters.json",
         "achieved HBM GB/s, Q6_K head 129280x7168 with q8_1 activations, rows 1..8",
         "int6 x int8 -> i32 dot4, f32 scales, bf16 out", _W002),
     "w8a8_silu": Workload(
-        5, "1,16,128", "fp8_gemv_kernel<W8A8> + quant_act_silu_e4m3_kernel (per call)",
-        ("fp8_gemv.hip", "quant.hip", "qhead_device.h"), "w8a8_silu_7168x18432_counters.json",
+        5, "1,16,128", "fp8_gemv_kernel<W8A8> + silu_slice_max/quant kernels (per call)",
+        ("fp8_gemv.hip", "silu_quant.hip", "quant_common.h", "qhead_device.h"),
+        "w8a8_silu_7168x18432_counters.json",
         "achieved HBM GB/s, W8A8 SiLU down projection 7168x18432, calls of 1/16/128 rows",
         "bf16 silu(gate)*up -> fp8e4m3 x fp8e4m3 -> f32 acc, bf16 out",
         "synthetic (seeded N(0,0.02) weights quantized per row on the device, gate N(0,1.5^2) "
         "and up N(0,1) BF16)"),
     "dequant": Workload(
-        4, "0", "dequant_nvfp4_bf16_kernel", ("dequant.hip", "qhead_device.h"),
+        4, "0", "dequant_fp4_kernel<false>", ("dequant.hip", "qhead_device.h"),
         "dequant_nvfp4_129280x7168_counters.json",
         "achieved HBM GB/s, load-time NVFP4 -> BF16 of the 129280x7168 head",
         "e2m1 x e4m3 x f32 global -> bf16", _W002),

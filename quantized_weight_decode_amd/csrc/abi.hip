@@ -158,7 +158,8 @@ int qhead_quant_act_e4m3(const uint16_t* x_bf16, int32_t rows, int32_t hidden, u
 
 size_t qhead_w8a8_workspace_bytes(int32_t hidden) {
     if (hidden <= 0) return 0;
-    return align256((size_t)128 * hidden) + align256(128 * sizeof(float));
+    return align256((size_t)128 * hidden) + align256(128 * sizeof(float)) +
+           align256((size_t)128 * kSiluMaxSlices * sizeof(uint32_t));
 }
 
 int qhead_w8a8_gemv(const uint8_t* w_e4m3, const float* row_scale, const uint8_t* xq,
@@ -259,10 +260,13 @@ int qhead_w8a8_silu(const uint8_t* w_e4m3, const float* row_scale, const uint16_
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* xq = static_cast<uint8_t*>(workspace);
     float* sa = reinterpret_cast<float*>(xq + align256((size_t)128 * hidden));
+    uint32_t* maxbuf =
+        reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(sa) + align256(128 * sizeof(float)));
     for (int32_t done = 0; done < rows;) {
         const int32_t m = (rows - done) < 128 ? (rows - done) : 128;
         const size_t off = (size_t)done * ld;
-        hipError_t e = run_quant_act_silu_e4m3(gate + off, up + off, ld, m, hidden, xq, sa, s);
+        hipError_t e = run_quant_act_silu_e4m3_split(gate + off, up + off, ld, m, hidden, xq, sa,
+                                                     maxbuf, s);
         if (e != hipSuccess) return QHEAD_ERR_HIP;
         for (int32_t g = 0; g < m;) {
             const int32_t gm = (m - g) < kW8A8GemvRows ? (m - g) : kW8A8GemvRows;

@@ -27,6 +27,10 @@ hipError_t run_quant_act_e4m3(const uint16_t* x, int rows, int H, uint8_t* xq, f
                               hipStream_t stream);
 hipError_t run_quant_act_silu_e4m3(const uint16_t* gate, const uint16_t* up, int ld, int rows,
                                    int H, uint8_t* xq, float* sa, hipStream_t stream);
+// Split over K-slices; maxbuf holds rows * kSiluMaxSlices words.
+hipError_t run_quant_act_silu_e4m3_split(const uint16_t* gate, const uint16_t* up, int ld,
+                                         int rows, int H, uint8_t* xq, float* sa,
+                                         uint32_t* maxbuf, hipStream_t stream);
 hipError_t run_silu_mul(const uint16_t* gate, const uint16_t* up, int64_t n, uint16_t* out,
                         const DeviceInfo& dev, hipStream_t stream);
 hipError_t run_quant_q8_1(const uint16_t* x, int rows, int H, uint8_t* q8, hipStream_t stream);
@@ -51,6 +55,7 @@ hipError_t run_q6k(const uint8_t* blocks, const uint8_t* q8, int R, int H, int V
                    const DeviceInfo& dev, hipStream_t stream);
 
 constexpr int kQ8BlockBytes = 36;
+constexpr int kSiluMaxSlices = 64;
 constexpr int kQ6KBlockBytes = 210;
 
 }  // namespace qh
