@@ -17,7 +17,7 @@ Other workloads, each on the 129280 x 7168 head (N(0, 0.02) weights
 quantized on the device):
   --workload w8a8     W8A8 calls of 1, 16 and 128 rows (activation
                       quantization + GEMV per call)
-  --workload nvfp4    NVFP4 W4A16 at rows 1, 2, 4, 8
+  --workload nvfp4    NVFP4 W4A16 at rows 1, 2, 4, 8, 16
   --workload q6k      Q6_K with q8_1 activations at rows 1, 2, 4, 8
   --workload dequant  load-time NVFP4 -> BF16 of the whole head
   --workload w8a8_silu  W8A8 down projection of bf16(silu(gate) * up), output
@@ -76,9 +76,9 @@ WORKLOADS = {
         "achieved HBM GB/s, W8A8 head 129280x7168, calls of 1/16/128 rows",
         "fp8e4m3 x fp8e4m3 -> f32 acc, bf16 out", _W002),
     "nvfp4": Workload(
-        4, "1,2,4,8", "nvfp4_gemv_kernel", ("nvfp4_gemv.hip", "qhead_device.h"),
+        4, "1,2,4,8,16", "nvfp4_gemv_kernel", ("nvfp4_gemv.hip", "qhead_device.h"),
         "nvfp4_gemv_129280x7168_counters.json",
-        "achieved HBM GB/s, NVFP4 W4A16 head 129280x7168, rows 1..8",
+        "achieved HBM GB/s, NVFP4 W4A16 head 129280x7168, rows 1..16",
         "e2m1 x e4m3 block scale x bf16 -> f32 acc, bf16 out", _W002),
     "q6k": Workload(
         4, "1,2,4,8", "q6k_gemv_kernel + quant_q8_1_kernel (per call)",

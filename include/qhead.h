@@ -12,7 +12,7 @@
  *                       quantized per row to E4M3 (qhead_quant_act_e4m3),
  *                       then an FP8 x FP8 dot, in <= 128-row calls.
  *   qhead_nvfp4         NVFP4: E2M1 nibbles, E4M3 scale per 16 weights,
- *                       F32 global multiplier (W4A16), <= 8 rows per pass.
+ *                       F32 global multiplier (W4A16), <= 16 rows per pass.
  *   qhead_q6k           Q6_K 210-byte super-blocks with activations first
  *                       quantized to q8_1 blocks (qhead_quant_q8_1), <= 8
  *                       rows per pass.
@@ -79,8 +79,9 @@ const char* qhead_status_string(int status);
 
 /* Rows one weight pass serves for `format`: 16 (FP8 W8A16, the multi-row
  * kernels of "lm_head_fp8_rows.rs" module doc), 128 (W8A8, W8A8_MAX_ROWS of
- * the same doc), 8 (NVFP4 narrow tiers, W4A16_BATCHM_WIDTHS of
- * "w4a16_gemv_tiers.rs"), 8 (Q6_K, MAX_M of "lm_head_q6k.rs"). Negative
+ * the same doc), 16 (NVFP4: the narrow tiers W4A16_BATCHM_WIDTHS and the
+ * 9..16-row batch16 tier of "w4a16_gemv_tiers.rs"), 8 (Q6_K, MAX_M of
+ * "lm_head_q6k.rs"). Negative
  * status for an unknown format. */
 int qhead_max_rows_per_launch(int32_t format);
 
@@ -176,7 +177,8 @@ int qhead_w8a8_silu(const uint8_t* w_e4m3, const float* row_scale, const uint16_
                     uint16_t* out_bf16, void* workspace, size_t workspace_bytes, void* stream);
 
 /* NVFP4 W4A16 head ("fp8_lut.rs" dequant_nvfp4_to_bf16 for the value
- * formula; "w4a16_gemv_tiers.rs" for the <= 8-row tiers):
+ * formula; "w4a16_gemv_tiers.rs" for the row tiers, here one weight pass per
+ * <= 16 rows):
  *   out[r][v] = bf16( fl32( global_scale * sum_b fl32(e4m3(bs[v][b]) * p_b) ) ),
  *   p_b = sum_{k in block b} x[r][k] * e2m1(nib(v,k)) in FP32,
  * blocks b of 16 consecutive k; nib(v,k) is the low nibble of

@@ -29,7 +29,7 @@ int max_rows(int32_t format) {
         case QHEAD_FMT_W8A8:
             return 128;
         case QHEAD_FMT_NVFP4:
-            return 8;
+            return 16;
         case QHEAD_FMT_Q6K:
             return 8;
         default:

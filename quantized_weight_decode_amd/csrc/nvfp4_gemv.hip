@@ -1,4 +1,4 @@
-// nvfp4_gemv.hip -- NVFP4 (W4A16) head GEMV for 1..8 activation rows on gfx950.
+// nvfp4_gemv.hip -- NVFP4 (W4A16) head GEMV for 1..16 activation rows on gfx950.
 //
 // out[r][v] = bf16( fl32( g * sum_b e4m3(bs[v][b]) * p_b ) ),
 // p_b = sum_{k in block b} x[r][k] * e2m1(nib(v,k)) in FP32,
@@ -6,26 +6,35 @@
 // k/2 for even k ("fp8_lut.rs": dequant_nvfp4_to_bf16's value E2M1 * E4M3
 // block scale * global multiplier, and the even-index-low-nibble order stated
 // for the dequant_nvfp4_bf16 kernel). The pages serve 4..8 rows with narrow
-// tiers ("w4a16_gemv_tiers.rs": W4A16_BATCHM_WIDTHS, select_tier); here every
-// row count 1..8 is its own instantiation, so no dead rows execute.
+// tiers and 9..16 rows with a wide one ("w4a16_gemv_tiers.rs":
+// W4A16_BATCHM_WIDTHS, select_tier, the batch16 kernel); here every row count
+// 1..16 is its own instantiation, so no dead rows execute.
 //
 // Same structure as the FP8 kernel: persistent workgroups, BF16 activations
-// staged in LDS per 8192-wide K-tile, bands of T vocab rows per wave, each
+// staged in LDS per K-tile (8192 wide up to 8 rows, 4096 above, so that the
+// rows fit in LDS), bands of T vocab rows per wave, each
 // lane streaming 16 packed bytes (32 weights, two scale blocks) per 2048-wide
 // segment with one coalesced non-temporal load plus a 2-byte block-scale
 // load. Nibbles become BF16 pairs with v_cvt_scalef32_pk_bf16_fp4 (exact),
 // block partials use v_dot2_f32_bf16, and each block partial is folded into
-// the row accumulator with one FMA by its decoded E4M3 block scale. The
-// cross-lane tree, tile order and per-lane order depend only on hidden, so
-// rows are bit-identical for every row count.
+// the row accumulator with one FMA by its decoded E4M3 block scale. Lanes
+// accumulate over groups of 4096 k (two segments) whatever the tile width;
+// each group's sum goes through one fixed cross-lane tree and the group sums
+// are added in k order. None of that depends on the row count, so rows are
+// bit-identical for every row count.
 #include "qhead_device.h"
 #include "qhead_internal.h"
 
 namespace qh {
 
-constexpr int kF4SegK = 2048;                    // k per segment: 64 lanes x 32
-constexpr int kF4TileK = 8192;                   // k per LDS tile
-constexpr int kF4VecPerTileRow = kF4TileK / 8;   // uint4 per activation row per tile
+constexpr int kF4SegK = 2048;    // k per segment: 64 lanes x 32
+constexpr int kF4GroupSegs = 2;  // segments per cross-lane reduction group (4096 k)
+
+// k per LDS tile for R rows: R * KT * 2 bytes must fit in LDS.
+template <int R>
+constexpr int f4_tile_k() {
+    return R <= 8 ? 8192 : 4096;
+}
 
 // LDS uint4 index of activations k_rel .. k_rel+7 in a tile row: segment s,
 // lane l (k 32l .. 32l+31 of the segment), quarter c (8 k each).
@@ -38,6 +47,7 @@ __device__ __forceinline__ int f4_lds_vec_index(int k_rel) {
 template <int R, int NTHREADS>
 __device__ __forceinline__ void f4_stage_tile(uint4* xs, const uint16_t* x, int H, int k0,
                                               int nseg) {
+    constexpr int kF4VecPerTileRow = f4_tile_k<R>() / 8;
     const int vec_per_row = nseg * (kF4SegK / 8);
     const int total = R * vec_per_row;
     for (int idx = threadIdx.x; idx < total; idx += NTHREADS) {
@@ -58,7 +68,10 @@ nvfp4_gemv_kernel(const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ bs
     constexpr int N = T * R;
     constexpr int NP = next_pow2(N);
     constexpr int M = Log2<NP>::value;
+    constexpr int kF4TileK = f4_tile_k<R>();
+    constexpr int kF4VecPerTileRow = kF4TileK / 8;
     static_assert(NP <= 64, "T*R must be <= 64");
+    static_assert(kF4TileK % (kF4GroupSegs * kF4SegK) == 0, "a tile holds whole groups");
     __shared__ uint4 xs[R * kF4VecPerTileRow];
 
     const int lane = threadIdx.x & 63;
@@ -119,7 +132,7 @@ nvfp4_gemv_kernel(const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ bs
                     const int ns = last ? s : ((s + 1 == nseg) ? 0 : s + 1);
                     load_item(nbi, ns, nxt);
                 }
-                if (s == 0) {
+                if (s % kF4GroupSegs == 0) {
 #pragma unroll
                     for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
                 }
@@ -215,11 +228,15 @@ nvfp4_gemv_kernel(const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ bs
                     }
                 }
                 }
-                if (s + 1 == nseg) {
+                if (s + 1 == nseg || (s + 1) % kF4GroupSegs == 0) {
+                    // end of a 4096-k group: one tree, then add in k order
                     wave_reduce_scatter<NP>(acc, lane);
+                    const bool first_group = tt == 0 && s < kF4GroupSegs;
 #pragma unroll
                     for (int j = 0; j < MAXB; ++j)
-                        if (j == bi) part[j] = (tt == 0) ? acc[0] : part[j] + acc[0];
+                        if (j == bi) part[j] = first_group ? acc[0] : part[j] + acc[0];
+                }
+                if (s + 1 == nseg) {
                     ++bi;
                     s = 0;
                 } else {
@@ -276,6 +293,14 @@ hipError_t run_nvfp4(const uint8_t* Wp, const uint8_t* bs, const uint16_t* x, fl
         QH_F4_CASE(6, 4, 8, 12, 1)
         QH_F4_CASE(7, 4, 8, 12, 1)
         QH_F4_CASE(8, 4, 8, 12, 1)
+        QH_F4_CASE(9, 4, 8, 12, 1)
+        QH_F4_CASE(10, 4, 8, 12, 1)
+        QH_F4_CASE(11, 4, 8, 12, 1)
+        QH_F4_CASE(12, 4, 8, 12, 1)
+        QH_F4_CASE(13, 4, 8, 12, 1)
+        QH_F4_CASE(14, 4, 8, 12, 1)
+        QH_F4_CASE(15, 4, 8, 12, 1)
+        QH_F4_CASE(16, 4, 8, 12, 1)
 #undef QH_F4_CASE
         default:
             return hipErrorInvalidValue;

@@ -1,7 +1,7 @@
 """C-ABI checks that need no GPU: the library loads, exports every function
 include/qhead.h declares, rejects invalid arguments before touching the
 device, and plans row chunks as the pages' chunk loops do (16 rows per FP8
-W8A16 pass, 128 per W8A8 call, 8 per NVFP4 / Q6_K pass)."""
+W8A16 pass, 128 per W8A8 call, 16 per NVFP4 pass, 8 per Q6_K pass)."""
 
 import ctypes
 import os
@@ -54,6 +54,7 @@ def test_plan_chunks(qh):
     assert qh.plan_chunks(qh.FMT_W8A8, 300) == [128, 128, 44]
     assert qh.plan_chunks(qh.FMT_W8A8, 128) == [128]
     assert qh.plan_chunks(qh.FMT_NVFP4, 8) == [8]
+    assert qh.plan_chunks(qh.FMT_NVFP4, 40) == [16, 16, 8]
     assert qh.plan_chunks(qh.FMT_Q6K, 13) == [8, 5]
     assert qh.plan_chunks(qh.FMT_Q6K, 0) == []
     L = qh.lib()
@@ -63,7 +64,7 @@ def test_plan_chunks(qh):
     # a short buffer still returns the full count and fills what fits
     assert L.qhead_plan_chunks(qh.FMT_FP8, 50, buf, 2) == 4
     assert list(buf) == [16, 16]
-    assert [qh.max_rows_per_launch(f) for f in range(4)] == [16, 128, 8, 8]
+    assert [qh.max_rows_per_launch(f) for f in range(4)] == [16, 128, 16, 8]
     assert L.qhead_max_rows_per_launch(7) == -5
 
 

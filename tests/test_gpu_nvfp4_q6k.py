@@ -91,20 +91,41 @@ def test_nvfp4_zero_global_scale(qh):
 
 
 def test_nvfp4_cfg4_full_head(qh):
+    """The 129280 x 7168 head at every row count 1..16 (one weight pass each:
+    8192-wide tiles up to 8 rows, 4096-wide above) and a 40-row call
+    (16 + 16 + 8); sampled logits within the bound, row-invariant bits."""
     wp, bs, g, wpd, bsd = nvfp4_head()
     cfg = synth.CONFIGS[4]
-    x = synth.activations_bf16(4, 8)
+    x = synth.activations_bf16(4, 40, max_rows=40)
     vidx = sample_vidx(cfg.vocab, 1500, 4)
     ref, ad = oracle.nvfp4_ref(wp, bs, g, x, vidx)
     outs = {}
-    for R in range(1, 9):
+    for R in list(range(1, 17)) + [40]:
         log(f"[case] nvfp4 cfg4 R={R}")
         out = qh.nvfp4(wpd, bsd, dev_bf16(x[:R]), g)
         torch.cuda.synchronize()
         outs[R] = host_bits(out)
         assert_within_bound(outs[R][:, vidx], ref[:R], ad[:R], f"nvfp4 cfg4 R={R}")
-    for R in range(1, 9):
-        assert np.array_equal(outs[R], outs[8][:R]), f"row invariance R={R}"
+    for R in outs:
+        assert np.array_equal(outs[R], outs[40][:R]), f"row invariance R={R}"
+
+
+@pytest.mark.parametrize("H", [2048, 6144, 10240, 16416])
+def test_nvfp4_row_invariance_across_tile_widths(qh, H):
+    """Hidden sizes whose 4096-k reduction groups split differently into the
+    8192-wide (<= 8 rows) and 4096-wide (9..16 rows) tiles."""
+    V = 700
+    wp, bs, g = _nvfp4_small(V, H)
+    x = synth.activations_bf16(4, 16, hidden=H, max_rows=16)
+    ref, ad = oracle.nvfp4_ref(wp, bs, g, x)
+    wpd, bsd = dev_u8(wp), dev_u8(bs)
+    outs = {}
+    for R in (1, 3, 8, 9, 16):
+        log(f"[case] nvfp4 tiles H={H} R={R}")
+        outs[R] = host_bits(qh.nvfp4(wpd, bsd, dev_bf16(x[:R]), g))
+        assert_within_bound(outs[R], ref[:R], ad[:R], f"nvfp4 H={H} R={R}")
+    for R in outs:
+        assert np.array_equal(outs[R], outs[16][:R]), f"row invariance H={H} R={R}"
 
 
 # ------------------------------------------------------------------- q8_1
