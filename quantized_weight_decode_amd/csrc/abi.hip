@@ -134,8 +134,9 @@ int qhead_fp8_rowscale(const uint8_t* w_e4m3, const float* row_scale, const uint
     DeviceInfo dev;
     if (int st = device_or_error(&dev)) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const int32_t chunk = max_rows(QHEAD_FMT_FP8);
     for (int32_t done = 0; done < rows;) {
-        const int32_t m = (rows - done) < 16 ? (rows - done) : 16;
+        const int32_t m = (rows - done) < chunk ? (rows - done) : chunk;
         hipError_t e = run_fp8_w8a16(w_e4m3, row_scale, x_bf16 + (size_t)done * hidden, m, hidden,
                                      vocab, out_bf16 + (size_t)done * vocab, dev, s);
         if (e != hipSuccess) return QHEAD_ERR_HIP;
@@ -202,7 +203,8 @@ int qhead_w8a8(const uint8_t* w_e4m3, const float* row_scale, const uint16_t* x_
     uint8_t* xq = static_cast<uint8_t*>(workspace);
     float* sa = reinterpret_cast<float*>(xq + align256((size_t)128 * hidden));
     for (int32_t done = 0; done < rows;) {
-        const int32_t m = (rows - done) < 128 ? (rows - done) : 128;
+        const int32_t m = (rows - done) < max_rows(QHEAD_FMT_W8A8) ? (rows - done)
+                                                                  : max_rows(QHEAD_FMT_W8A8);
         hipError_t e = run_quant_act_e4m3(x_bf16 + (size_t)done * hidden, m, hidden, xq, sa, s);
         if (e != hipSuccess) return QHEAD_ERR_HIP;
         for (int32_t g = 0; g < m;) {
@@ -263,7 +265,8 @@ int qhead_w8a8_silu(const uint8_t* w_e4m3, const float* row_scale, const uint16_
     uint32_t* maxbuf =
         reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(sa) + align256(128 * sizeof(float)));
     for (int32_t done = 0; done < rows;) {
-        const int32_t m = (rows - done) < 128 ? (rows - done) : 128;
+        const int32_t m = (rows - done) < max_rows(QHEAD_FMT_W8A8) ? (rows - done)
+                                                                  : max_rows(QHEAD_FMT_W8A8);
         const size_t off = (size_t)done * ld;
         hipError_t e = run_quant_act_silu_e4m3_split(gate + off, up + off, ld, m, hidden, xq, sa,
                                                      maxbuf, s);
@@ -292,8 +295,9 @@ int qhead_nvfp4(const uint8_t* w_packed, const uint8_t* block_scale, const uint1
     DeviceInfo dev;
     if (int st = device_or_error(&dev)) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const int32_t chunk = max_rows(QHEAD_FMT_NVFP4);
     for (int32_t done = 0; done < rows;) {
-        const int32_t m = (rows - done) < 8 ? (rows - done) : 8;
+        const int32_t m = (rows - done) < chunk ? (rows - done) : chunk;
         hipError_t e = run_nvfp4(w_packed, block_scale, x_bf16 + (size_t)done * hidden,
                                  global_scale, m, hidden, vocab,
                                  out_bf16 + (size_t)done * vocab, dev, s);
@@ -330,8 +334,9 @@ int qhead_q6k_gemv(const uint8_t* blocks, const void* q8, int32_t rows, int32_t 
     if (int st = device_or_error(&dev)) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t q8_row = (size_t)(hidden / 32) * kQ8BlockBytes;
+    const int32_t chunk = max_rows(QHEAD_FMT_Q6K);
     for (int32_t done = 0; done < rows;) {
-        const int32_t m = (rows - done) < 8 ? (rows - done) : 8;
+        const int32_t m = (rows - done) < chunk ? (rows - done) : chunk;
         hipError_t e = run_q6k(blocks, static_cast<const uint8_t*>(q8) + (size_t)done * q8_row, m,
                                hidden, vocab, out_bf16 + (size_t)done * vocab, dev, s);
         if (e != hipSuccess) return QHEAD_ERR_HIP;
@@ -356,8 +361,9 @@ int qhead_q6k(const uint8_t* blocks, const void* scales, const uint16_t* x_bf16,
     if (int st = device_or_error(&dev)) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* q8 = static_cast<uint8_t*>(workspace);
+    const int32_t chunk = max_rows(QHEAD_FMT_Q6K);
     for (int32_t done = 0; done < rows;) {
-        const int32_t m = (rows - done) < 8 ? (rows - done) : 8;
+        const int32_t m = (rows - done) < chunk ? (rows - done) : chunk;
         hipError_t e = run_quant_q8_1(x_bf16 + (size_t)done * hidden, m, hidden, q8, s);
         if (e != hipSuccess) return QHEAD_ERR_HIP;
         e = run_q6k(blocks, q8, m, hidden, vocab, out_bf16 + (size_t)done * vocab, dev, s);
