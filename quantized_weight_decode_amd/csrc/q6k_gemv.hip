@@ -82,8 +82,10 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     static_assert(NP <= 64 && R <= 8, "T*R must be <= 64, R <= 8");
     static_assert(kItemBytes + 15 <= 64 * 16, "an item must fit one 16-byte load per lane");
     __shared__ Q6Lds<R> L;
-    // wave-private weight staging: [wave][buffer][row t][1024 bytes]
-    __shared__ u32x4_t WB[WAVES][2][T][kWave];
+    // wave-private weight staging: [wave][row t][1024 bytes]. One buffer is
+    // enough: a wave's LDS instructions execute in order, so the item written
+    // after the current item's reads never overtakes them.
+    __shared__ u32x4_t WB[WAVES][T][kWave];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -93,10 +95,12 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     const int NT = (H + kQTileK - 1) / kQTileK;
     const int nsb = H / 256;
     const size_t rowbytes = (size_t)nsb * kQ6KBlockBytes;
-    const uintptr_t base_addr = reinterpret_cast<uintptr_t>(blocks);
 
-    // lane -> (super-block within the item, sub-block t = 8n + 2c + h)
-    const int sbi = lane >> 4;
+    // lane -> (super-block within the item, sub-block t = 8n + 2c + h). Half
+    // waves take super-blocks {0, 2} and {1, 3}: those two start 105 dwords
+    // apart, so their fields fall in different LDS bank groups (0 and 1,
+    // 52.5 dwords apart, would share them).
+    const int sbi = (((lane >> 4) & 1) << 1) | (lane >> 5);
     const int t16 = lane & 15;
     const int n = t16 >> 3, c = (t16 >> 1) & 3, h = t16 & 1;
     const int ql_off = 64 * n + 32 * (c & 1) + 16 * h;
@@ -128,12 +132,13 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
             const int nbb = first < NB ? min(MAXB, (NB - 1 - first) / TW + 1) : 0;
             const int nitems = nbb * nseg;
 
-            // Absolute address of the first byte of item (bi, s) in row t;
-            // rows past the vocab tail re-read the last row (never stored).
-            auto item_addr = [&](int bi, int s, int t) -> uintptr_t {
+            // First byte of item (bi, s) in row t (rows past the vocab tail
+            // re-read the last row, never stored). Kept as a pointer into
+            // `blocks` so the loads stay global (not flat) loads.
+            auto item_ptr = [&](int bi, int s, int t) -> const uint8_t* {
                 const int v = min(((sj * MAXB + bi) * TW + gw) * T + t, V - 1);
                 const int sb0 = tt * kQSbPerTile + s * 4;
-                return base_addr + (size_t)v * rowbytes + (size_t)sb0 * kQ6KBlockBytes;
+                return blocks + (size_t)v * rowbytes + (size_t)sb0 * kQ6KBlockBytes;
             };
             // One 16-byte aligned chunk per lane; lanes past the item's last
             // chunk re-read it.
@@ -142,23 +147,23 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                 const int nbytes = min(4, nsb - sb0) * kQ6KBlockBytes;
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
-                    const uintptr_t a = item_addr(bi, s, t);
-                    const uintptr_t a16 = a & ~(uintptr_t)15;
-                    const int last = (int)(((a + nbytes - 1) & ~(uintptr_t)15) - a16) >> 4;
-                    const int ch = min(lane, last);
-                    g[t] = *reinterpret_cast<const u32x4_t*>(a16 + 16 * (uintptr_t)ch);
+                    const uint8_t* p = item_ptr(bi, s, t);
+                    const int mis = (int)(reinterpret_cast<uintptr_t>(p) & 15);
+                    const uint8_t* p16 = p - mis;
+                    const int ch = min(lane, (mis + nbytes - 1) >> 4);
+                    g[t] = *reinterpret_cast<const u32x4_t*>(p16 + 16 * ch);
                 }
             };
-            auto stage = [&](int buf, const u32x4_t (&g)[T]) {
+            auto stage = [&](const u32x4_t (&g)[T]) {
 #pragma unroll
-                for (int t = 0; t < T; ++t) WB[wave][buf][t][lane] = g[t];
+                for (int t = 0; t < T; ++t) WB[wave][t][lane] = g[t];
             };
 
             float acc[NP];
             int bi = 0, s = 0;
-            // Item `it` is in LDS buffer `buf`; item it + 1 is in flight in
-            // `gn`; `gf` is free and receives item it + 2.
-            auto step = [&](int it, int buf, u32x4_t (&gf)[T], const u32x4_t (&gn)[T]) {
+            // Item `it` is in LDS; item it + 1 is in flight in `gn`; `gf` is
+            // free and receives item it + 2.
+            auto step = [&](int it, u32x4_t (&gf)[T], const u32x4_t (&gn)[T]) {
                 // (bi, s) of items it + 1 and it + 2, clamped to the last item
                 int bi1 = bi, s1 = s;
                 if (it + 1 < nitems) { if (++s1 == nseg) { s1 = 0; ++bi1; } }
@@ -175,10 +180,10 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                 float wsc[T];
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
-                    const uintptr_t a = item_addr(bi, s, t);
+                    const uintptr_t a = reinterpret_cast<uintptr_t>(item_ptr(bi, s, t));
                     const int rel = (int)(a & 15) + sbi * kQ6KBlockBytes;  // LDS byte offset
                     const uint32_t sh = (uint32_t)(rel & 3);
-                    const uint8_t* lb = reinterpret_cast<const uint8_t*>(&WB[wave][buf][t][0]);
+                    const uint8_t* lb = reinterpret_cast<const uint8_t*>(&WB[wave][t][0]);
                     const uint32_t* lw = reinterpret_cast<const uint32_t*>(lb + (rel & ~3));
                     uint32_t qlw[5], qhw[5];
 #pragma unroll
@@ -214,8 +219,8 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                         acc[r * T + t] = __builtin_fmaf((float)is, wsc[t] * d8, acc[r * T + t]);
                     }
                 }
-                // item it + 1 into the other buffer (its last reader was item it - 1)
-                stage(buf ^ 1, gn);
+                // item it + 1 replaces item it (after all of item it's reads)
+                stage(gn);
                 if (s + 1 == nseg) {
                     wave_reduce_scatter<NP>(acc, lane);
 #pragma unroll
@@ -230,15 +235,15 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
             u32x4_t gA[T], gB[T];
             if (nitems > 0) {
                 issue(0, 0, gA);
-                stage(0, gA);
+                stage(gA);
                 int bi1 = 0, s1 = 0;
                 if (nitems > 1) { if (++s1 == nseg) { s1 = 0; ++bi1; } }
                 issue(bi1, s1, gB);
             }
 #pragma unroll 1
             for (int it = 0; it < nitems; it += 2) {
-                step(it, 0, gA, gB);
-                if (it + 1 < nitems) step(it + 1, 1, gB, gA);
+                step(it, gA, gB);
+                if (it + 1 < nitems) step(it + 1, gB, gA);
             }
         }
 
@@ -271,9 +276,9 @@ hipError_t run_q6k(const uint8_t* blocks, const uint8_t* q8, int R, int H, int V
 #define QH_Q6_CASE(RR, TT, WV, MB, BPC) \
     case RR:                            \
         return launch_q6k<RR, TT, WV, MB, BPC>(blocks, q8, H, V, out, dev, stream);
-        QH_Q6_CASE(1, 4, 8, 12, 2)
-        QH_Q6_CASE(2, 4, 8, 12, 1)
-        QH_Q6_CASE(3, 4, 8, 12, 1)
+        QH_Q6_CASE(1, 4, 16, 12, 1)
+        QH_Q6_CASE(2, 2, 16, 12, 1)
+        QH_Q6_CASE(3, 2, 16, 12, 1)
         QH_Q6_CASE(4, 4, 8, 12, 1)
         QH_Q6_CASE(5, 4, 8, 12, 1)
         QH_Q6_CASE(6, 4, 8, 12, 1)
