@@ -43,6 +43,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+import synth  # noqa: E402  (seeded input shapes; no method arithmetic)
+
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "quantized_weight_decode_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -64,30 +66,34 @@ class Workload:
 _W002 = "synthetic (seeded N(0,0.02) weights quantized on the device, N(0,1) BF16 x)"
 WORKLOADS = {
     "fp8": Workload(
-        2, "1,2,4,8,16", "fp8_gemv_kernel", ("fp8_gemv.hip", "qhead_device.h"),
+        synth.FP8_155136X8192, "1,2,4,8,16", "fp8_gemv_kernel",
+        ("fp8_gemv.hip", "qhead_device.h"),
         "fp8_gemv_155136x8192_counters.json",
         "achieved HBM GB/s (% of peak) & logits rows/sec, 1.27 GB FP8 head, rows 1..16",
         "fp8e4m3 x bf16 -> f32 acc, bf16 out",
         "synthetic (seeded N(0,0.015) weights quantized per row to E4M3, N(0,1) BF16 x)"),
     "w8a8": Workload(
-        3, "1,16,128", "fp8_gemv_kernel<W8A8> + quant_act_e4m3_kernel (per call)",
+        synth.W8A8_129280X7168, "1,16,128",
+        "fp8_gemv_kernel<W8A8> + quant_act_e4m3_kernel (per call)",
         ("fp8_gemv.hip", "act_quant.hip", "quant_common.h", "qhead_device.h"),
         "w8a8_129280x7168_counters.json",
         "achieved HBM GB/s, W8A8 head 129280x7168, calls of 1/16/128 rows",
         "fp8e4m3 x fp8e4m3 -> f32 acc, bf16 out", _W002),
     "nvfp4": Workload(
-        4, "1,2,4,8,16", "nvfp4_gemv_kernel", ("nvfp4_gemv.hip", "qhead_device.h"),
+        synth.NVFP4_Q6K_129280X7168, "1,2,4,8,16", "nvfp4_gemv_kernel",
+        ("nvfp4_gemv.hip", "qhead_device.h"),
         "nvfp4_gemv_129280x7168_counters.json",
         "achieved HBM GB/s, NVFP4 W4A16 head 129280x7168, rows 1..16",
         "e2m1 x e4m3 block scale x bf16 -> f32 acc, bf16 out", _W002),
     "q6k": Workload(
-        4, "1,2,4,8", "q6k_gemv_kernel + quant_q8_1_kernel (per call)",
+        synth.NVFP4_Q6K_129280X7168, "1,2,4,8", "q6k_gemv_kernel + quant_q8_1_kernel (per call)",
         ("q6k_gemv.hip", "act_quant.hip", "quant_common.h", "qhead_device.h"),
         "q6k_gemv_129280x7168_counters.json",
         "achieved HBM GB/s, Q6_K head 129280x7168 with q8_1 activations, rows 1..8",
         "int6 x int8 -> i32 dot4, f32 scales, bf16 out", _W002),
     "w8a8_silu": Workload(
-        5, "1,16,128", "fp8_gemv_kernel<W8A8> + silu_slice_max/quant kernels (per call)",
+        synth.SILU_DOWN_7168X18432, "1,16,128",
+        "fp8_gemv_kernel<W8A8> + silu_slice_max/quant kernels (per call)",
         ("fp8_gemv.hip", "silu_quant.hip", "quant_common.h", "qhead_device.h"),
         "w8a8_silu_7168x18432_counters.json",
         "achieved HBM GB/s, W8A8 SiLU down projection 7168x18432, calls of 1/16/128 rows",
@@ -95,7 +101,8 @@ WORKLOADS = {
         "synthetic (seeded N(0,0.02) weights quantized per row on the device, gate N(0,1.5^2) "
         "and up N(0,1) BF16)"),
     "dequant": Workload(
-        4, "0", "dequant_fp4_kernel<false>", ("dequant.hip", "qhead_device.h"),
+        synth.NVFP4_Q6K_129280X7168, "0", "dequant_fp4_kernel<false>",
+        ("dequant.hip", "qhead_device.h"),
         "dequant_nvfp4_129280x7168_counters.json",
         "achieved HBM GB/s, load-time NVFP4 -> BF16 of the 129280x7168 head",
         "e2m1 x e4m3 x f32 global -> bf16", _W002),
@@ -133,8 +140,6 @@ def nvfp4_global(amax: float) -> float:
 
 def build_head(name: str, cfg, qh, torch):
     """Generate the seeded head chunk by chunk and quantize it on the device."""
-    import synth
-
     dev = torch.device("cuda:0")
     V, H = cfg.vocab, cfg.hidden
     if name in ("fp8", "w8a8", "w8a8_silu"):
@@ -245,7 +250,7 @@ def cpu_baseline(name: str, cfg, rows: list[int], target_s: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the head shards by vocab across GPUs; see the design notes)", file=sys.stderr)
         sys.exit(2)
 

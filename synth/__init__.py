@@ -6,26 +6,32 @@ generator and rounds the activations to BF16 through torch's CPU cast.
 Quantizing the drawn weights (to E4M3 rows, NVFP4 blocks or Q6_K super-blocks)
 is the job of whoever consumes them.
 
-Workload shapes follow the five head configurations this library is measured
-on (the FP8 head of "lm_head_fp8_rows.rs", the W8A8 head of "w8a8_layer.rs",
-the NVFP4 head of "w4a16_gemv_tiers.rs" and the Q6_K head of "lm_head_q6k.rs"):
+Workload shapes follow the head configurations this library is measured on
+(the FP8 head of "lm_head_fp8_rows.rs", the W8A8 head of "w8a8_layer.rs",
+the NVFP4 head of "w4a16_gemv_tiers.rs" and the Q6_K head of "lm_head_q6k.rs",
+and the SiLU FFN down projection of "w8a8_layer.rs"); each has a seed id:
 
-  cfg0  FP8 W8A16  vocab 8192   x hidden 1024, W ~ N(0, 0.02)
-  cfg1  FP8 W8A16  vocab 32000  x hidden 4096, W ~ N(0, 0.02), x with 41
-        outlier channels scaled x20
-  cfg2  FP8 W8A16  vocab 155136 x hidden 8192, W ~ N(0, 0.015) (1.27 GB head)
-  cfg3  W8A8       vocab 129280 x hidden 7168, W ~ N(0, 0.02)
-  cfg4  NVFP4 / Q6_K vocab 129280 x hidden 7168, W ~ N(0, 0.02)
-  cfg5  W8A8 SiLU down projection: output 7168 x FFN width 18432,
-        W ~ N(0, 0.02); gate ~ N(0, 1.5^2), up ~ N(0, 1) (the FFN's
-        activation is bf16(silu(gate) * up), "w8a8_layer.rs" silu_proj)
+  FP8_8192X1024          id 0  FP8 W8A16, vocab 8192 x hidden 1024,
+                               W ~ N(0, 0.02)
+  FP8_32000X4096         id 1  FP8 W8A16, vocab 32000 x hidden 4096,
+                               W ~ N(0, 0.02), x with 41 outlier channels
+                               scaled x20
+  FP8_155136X8192        id 2  FP8 W8A16, vocab 155136 x hidden 8192,
+                               W ~ N(0, 0.015) (the 1.27 GB head)
+  W8A8_129280X7168       id 3  W8A8, vocab 129280 x hidden 7168, W ~ N(0, 0.02)
+  NVFP4_Q6K_129280X7168  id 4  NVFP4 / Q6_K, vocab 129280 x hidden 7168,
+                               W ~ N(0, 0.02)
+  SILU_DOWN_7168X18432   id 5  W8A8 SiLU down projection: output 7168 x FFN
+                               width 18432, W ~ N(0, 0.02); gate
+                               ~ N(0, 1.5^2), up ~ N(0, 1) (the FFN's
+                               activation is bf16(silu(gate) * up))
 
-Weights are drawn in independent 1024-row chunks, chunk c of config i seeded
-with SeedSequence([100 + i, c]), so any vocab row range can be regenerated on
-its own. Activations for config i use seed 200 + i and are drawn once for the
-configuration's largest row count; a smaller row count takes the leading rows.
-The outlier channels of cfg1 are drawn with seed 300 + i; the gate and up
-rows of cfg5 with seeds 400 + i and 500 + i.
+Weights are drawn in independent 1024-row chunks, chunk c of the
+configuration with id i seeded with SeedSequence([100 + i, c]), so any vocab
+row range can be regenerated on its own. Activations for id i use seed
+200 + i and are drawn once for the configuration's largest row count; a
+smaller row count takes the leading rows. The outlier channels use seed
+300 + i; the SiLU gate and up rows seeds 400 + i and 500 + i.
 """
 
 from __future__ import annotations
@@ -51,18 +57,29 @@ class HeadConfig:
     label: str = field(default="")
 
 
+FP8_8192X1024 = 0
+FP8_32000X4096 = 1
+FP8_155136X8192 = 2
+W8A8_129280X7168 = 3
+NVFP4_Q6K_129280X7168 = 4
+SILU_DOWN_7168X18432 = 5
+
 CONFIGS = {
-    0: HeadConfig(0, "fp8", 8192, 1024, 0.02, (1,), 0, "fp8 head 8192x1024"),
-    1: HeadConfig(1, "fp8", 32000, 4096, 0.02, (1, 2, 3, 4, 8, 16, 40), 41,
-                  "fp8 head 32000x4096, outlier channels"),
-    2: HeadConfig(2, "fp8", 155136, 8192, 0.015, (1, 2, 4, 8, 16, 64), 0,
-                  "fp8 head 155136x8192 (1.27 GB)"),
-    3: HeadConfig(3, "w8a8", 129280, 7168, 0.02, (1, 16, 128, 300), 0,
-                  "w8a8 head 129280x7168"),
-    4: HeadConfig(4, "nvfp4q6k", 129280, 7168, 0.02, (1, 2, 3, 4, 5, 6, 7, 8), 0,
-                  "nvfp4 / q6_k head 129280x7168"),
-    5: HeadConfig(5, "w8a8silu", 7168, 18432, 0.02, (1, 16, 128, 130), 0,
-                  "w8a8 silu down projection 7168x18432"),
+    FP8_8192X1024: HeadConfig(FP8_8192X1024, "fp8", 8192, 1024, 0.02, (1,), 0,
+                              "fp8 head 8192x1024"),
+    FP8_32000X4096: HeadConfig(FP8_32000X4096, "fp8", 32000, 4096, 0.02,
+                               (1, 2, 3, 4, 8, 16, 40), 41,
+                               "fp8 head 32000x4096, outlier channels"),
+    FP8_155136X8192: HeadConfig(FP8_155136X8192, "fp8", 155136, 8192, 0.015,
+                                (1, 2, 4, 8, 16, 64), 0, "fp8 head 155136x8192 (1.27 GB)"),
+    W8A8_129280X7168: HeadConfig(W8A8_129280X7168, "w8a8", 129280, 7168, 0.02,
+                                 (1, 16, 128, 300), 0, "w8a8 head 129280x7168"),
+    NVFP4_Q6K_129280X7168: HeadConfig(NVFP4_Q6K_129280X7168, "nvfp4q6k", 129280, 7168, 0.02,
+                                      (1, 2, 3, 4, 5, 6, 7, 8), 0,
+                                      "nvfp4 / q6_k head 129280x7168"),
+    SILU_DOWN_7168X18432: HeadConfig(SILU_DOWN_7168X18432, "w8a8silu", 7168, 18432, 0.02,
+                                     (1, 16, 128, 130), 0,
+                                     "w8a8 silu down projection 7168x18432"),
 }
 
 

@@ -86,16 +86,16 @@ def fp8_head(cfg_index: int):
 def nvfp4_head():
     """Host (packed, block scales, g) and device copies of the full NVFP4 head
     of the 129280 x 7168 config."""
-    log("[prep] nvfp4 head cfg4")
-    wp, bs, g = oracle.prep_config_weights(4, "nvfp4")
+    log("[prep] nvfp4 head 129280x7168")
+    wp, bs, g = oracle.prep_config_weights(synth.NVFP4_Q6K_129280X7168, "nvfp4")
     return wp, bs, g, dev_u8(wp), dev_u8(bs)
 
 
 @functools.lru_cache(maxsize=1)
 def q6k_head():
     """Host and device copies of the full Q6_K head of the 129280 x 7168 config."""
-    log("[prep] q6k head cfg4")
-    blocks = oracle.prep_config_weights(4, "q6k")
+    log("[prep] q6k head 129280x7168")
+    blocks = oracle.prep_config_weights(synth.NVFP4_Q6K_129280X7168, "q6k")
     return blocks, dev_u8(blocks)
 
 

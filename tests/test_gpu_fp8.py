@@ -12,8 +12,8 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import (DEV, assert_within_bound, bf16_bits_to_f64, dev_bf16, dev_f32, dev_u8, fp8_head,
-                         host_bits, log, sample_vidx, x_rows)
+from gpu_helpers import (DEV, assert_within_bound, bf16_bits_to_f64, dev_bf16, dev_f32, dev_u8,
+                         fp8_head, host_bits, log, sample_vidx, x_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +26,7 @@ def qh():
     return m
 
 
-def _fp8_small(V, H, cfg=0, seed_rows=None):
+def _fp8_small(V, H, cfg=synth.FP8_8192X1024, seed_rows=None):
     wf = synth.weight_rows_f32(cfg, 0, V, vocab=V, hidden=H)
     return oracle.prep_fp8_rows(wf)
 
@@ -74,20 +74,20 @@ def test_fp8_exact_dyadic_cases_bit_exact(qh):
     assert np.array_equal(host_bits(out), oracle.bf16_rne_array(ref))
 
 
-# ------------------------------------------------------------------ cfg0
+# ------------------------------------------------------------------ 8192x1024
 
-def test_fp8_cfg0_all_logits(qh):
+def test_fp8_8192x1024_all_logits(qh):
     w, s = _fp8_small(8192, 1024)
-    x = x_rows(0, 16, max_rows=16)
+    x = x_rows(synth.FP8_8192X1024, 16, max_rows=16)
     wd, sd = dev_u8(w), dev_f32(s)
     ref, ad = oracle.fp8_rowscale_ref(w, s, x)
     outs = {}
     for R in range(1, 17):
-        log(f"[case] fp8 cfg0 R={R}")
+        log(f"[case] fp8 8192x1024 R={R}")
         out = qh.fp8_rowscale(wd, sd, dev_bf16(x[:R]))
         torch.cuda.synchronize()
         outs[R] = host_bits(out)
-        assert_within_bound(outs[R], ref[:R], ad[:R], f"cfg0 R={R}")
+        assert_within_bound(outs[R], ref[:R], ad[:R], f"8192x1024 R={R}")
     # row invariance: a row's bits do not depend on the launch's row count
     for R in range(1, 17):
         assert np.array_equal(outs[R], outs[16][:R]), R
@@ -99,9 +99,10 @@ def test_fp8_edge_shapes(qh):
     for V, H, rows in [(1001, 1040, 3), (1, 16, 2), (37, 16, 16), (513, 4112, 17),
                        (300, 8208, 9), (4099, 3072, 33), (64, 8192, 1)]:
         log(f"[case] fp8 edge V={V} H={H} rows={rows}")
-        wf = synth.weight_rows_f32(1, 0, V, vocab=V, hidden=H)
+        wf = synth.weight_rows_f32(synth.FP8_32000X4096, 0, V, vocab=V, hidden=H)
         w, s = oracle.prep_fp8_rows(wf)
-        x = synth.activations_bf16(1, rows, hidden=H, max_rows=rows, outlier_channels=0)
+        x = synth.activations_bf16(synth.FP8_32000X4096, rows, hidden=H, max_rows=rows,
+                                   outlier_channels=0)
         out = qh.fp8_rowscale(dev_u8(w), dev_f32(s), dev_bf16(x))
         torch.cuda.synchronize()
         ref, ad = oracle.fp8_rowscale_ref(w, s, x)
@@ -123,7 +124,7 @@ def test_fp8_zero_rows_and_scale(qh):
     w[5] = 0
     s[5] = 0.0
     s[9] = 0.0
-    x = x_rows(0, 3, hidden=H, max_rows=3)
+    x = x_rows(synth.FP8_8192X1024, 3, hidden=H, max_rows=3)
     x[1] = 0
     out = host_bits(qh.fp8_rowscale(dev_u8(w), dev_f32(s), dev_bf16(x)))
     torch.cuda.synchronize()
@@ -131,41 +132,41 @@ def test_fp8_zero_rows_and_scale(qh):
     assert (vals[:, 5] == 0).all() and (vals[:, 9] == 0).all() and (out[1] == 0).all()
 
 
-# ------------------------------------------------------------------ cfg1
+# ------------------------------------------------------------------ 32000x4096
 
-def test_fp8_cfg1_outliers_sampled(qh):
-    w, s, wd, sd = fp8_head(1)
-    cfg = synth.CONFIGS[1]
-    x = x_rows(1, 40)
+def test_fp8_32000x4096_outliers_sampled(qh):
+    w, s, wd, sd = fp8_head(synth.FP8_32000X4096)
+    cfg = synth.CONFIGS[synth.FP8_32000X4096]
+    x = x_rows(synth.FP8_32000X4096, 40)
     vidx = sample_vidx(cfg.vocab, 3000, 1)
     ref, ad = oracle.fp8_rowscale_ref(w, s, x, vidx)
     outs = {}
     for R in cfg.rows:
-        log(f"[case] fp8 cfg1 R={R}")
+        log(f"[case] fp8 32000x4096 R={R}")
         out = qh.fp8_rowscale(wd, sd, dev_bf16(x[:R]))
         torch.cuda.synchronize()
         outs[R] = host_bits(out)
-        assert_within_bound(outs[R][:, vidx], ref[:R], ad[:R], f"cfg1 R={R}")
+        assert_within_bound(outs[R][:, vidx], ref[:R], ad[:R], f"32000x4096 R={R}")
     for R in cfg.rows:
         assert np.array_equal(outs[R], outs[40][:R]), f"row invariance R={R}"
 
 
-# ------------------------------------------------------------------ cfg2
+# ------------------------------------------------------------------ 155136x8192
 
-def test_fp8_cfg2_full_head_sampled(qh):
+def test_fp8_155136x8192_full_head_sampled(qh):
     """The 1.27 GB head at rows 1, 2, 4, 8, 16 and 64 (four 16-row passes)."""
-    w, s, wd, sd = fp8_head(2)
-    cfg = synth.CONFIGS[2]
-    x = x_rows(2, 64)
+    w, s, wd, sd = fp8_head(synth.FP8_155136X8192)
+    cfg = synth.CONFIGS[synth.FP8_155136X8192]
+    x = x_rows(synth.FP8_155136X8192, 64)
     vidx = sample_vidx(cfg.vocab, 1500, 2)
     ref, ad = oracle.fp8_rowscale_ref(w, s, x, vidx)
     outs = {}
     for R in cfg.rows:
-        log(f"[case] fp8 cfg2 R={R}")
+        log(f"[case] fp8 155136x8192 R={R}")
         out = qh.fp8_rowscale(wd, sd, dev_bf16(x[:R]))
         torch.cuda.synchronize()
         outs[R] = host_bits(out)
-        assert_within_bound(outs[R][:, vidx], ref[:R], ad[:R], f"cfg2 R={R}")
+        assert_within_bound(outs[R][:, vidx], ref[:R], ad[:R], f"155136x8192 R={R}")
     for R in cfg.rows:
         assert np.array_equal(outs[R], outs[64][:R]), f"row invariance R={R}"
     # the 64-row call equals its four 16-row chunks launched separately
@@ -176,7 +177,7 @@ def test_fp8_cfg2_full_head_sampled(qh):
 
 def test_quantize_fp8_rows_matches_oracle(qh):
     """Load-time weight quantization on the GPU equals the oracle's bytes."""
-    wf = synth.weight_rows_f32(2, 5000, 7048)
+    wf = synth.weight_rows_f32(synth.FP8_155136X8192, 5000, 7048)
     wf[3] = 0.0
     log("[case] quantize_fp8_rows 2048x8192")
     codes, scales = qh.quantize_fp8_rows(dev_f32(wf))
@@ -188,7 +189,7 @@ def test_quantize_fp8_rows_matches_oracle(qh):
 
 # --------------------------------------------------------- act quant, W8A8
 
-def _act_rows_with_specials(H, rows, cfg=3):
+def _act_rows_with_specials(H, rows, cfg=synth.W8A8_129280X7168):
     x = synth.activations_bf16(cfg, rows, hidden=H, max_rows=rows)
     x[0] = 0                       # all-zero row
     x[1] = 0x8000                  # all negative zero
@@ -242,23 +243,23 @@ def test_w8a8_exact_cases_bit_exact(qh):
     assert np.array_equal(host_bits(out), oracle.bf16_rne_array(ref))
 
 
-def test_w8a8_cfg3_full_head(qh):
+def test_w8a8_129280x7168_full_head(qh):
     """W8A8 on the 129280 x 7168 head at rows 1, 16, 128 and 300 (<= 128-row
     calls); logits within the bound on sampled vocab rows, row-invariant bits."""
-    w, s, wd, sd = fp8_head(3)
-    cfg = synth.CONFIGS[3]
-    x = x_rows(3, 300)
+    w, s, wd, sd = fp8_head(synth.W8A8_129280X7168)
+    cfg = synth.CONFIGS[synth.W8A8_129280X7168]
+    x = x_rows(synth.W8A8_129280X7168, 300)
     xq, sa = oracle.quant_act_e4m3(x)
     vidx = sample_vidx(cfg.vocab, 800, 3)
     ref, ad = oracle.w8a8_ref(w, s, xq, sa, vidx)
     ws = qh.w8a8_workspace(cfg.hidden, DEV)
     outs = {}
     for R in cfg.rows:
-        log(f"[case] w8a8 cfg3 R={R}")
+        log(f"[case] w8a8 129280x7168 R={R}")
         out = qh.w8a8(wd, sd, dev_bf16(x[:R]), workspace=ws)
         torch.cuda.synchronize()
         outs[R] = host_bits(out)
-        assert_within_bound(outs[R][:, vidx], ref[:R], ad[:R], f"cfg3 R={R}")
+        assert_within_bound(outs[R][:, vidx], ref[:R], ad[:R], f"129280x7168 R={R}")
     for R in cfg.rows:
         assert np.array_equal(outs[R], outs[300][:R]), f"row invariance R={R}"
     # rows 128..255 of the 300-row call equal a separate call on those rows
@@ -270,8 +271,8 @@ def test_w8a8_two_streams_two_workspaces(qh):
     V, H = 4096, 2048
     w, s = _fp8_small(V, H)
     wd, sd = dev_u8(w), dev_f32(s)
-    xa = x_rows(3, 20, hidden=H, max_rows=40)
-    xb = synth.to_bf16_bits(synth.activations_f32(3, 40, hidden=H)[20:40] * 3)
+    xa = x_rows(synth.W8A8_129280X7168, 20, hidden=H, max_rows=40)
+    xb = synth.to_bf16_bits(synth.activations_f32(synth.W8A8_129280X7168, 40, hidden=H)[20:40] * 3)
     ref_a = host_bits(qh.w8a8(wd, sd, dev_bf16(xa)))
     ref_b = host_bits(qh.w8a8(wd, sd, dev_bf16(xb)))
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()

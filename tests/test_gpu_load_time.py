@@ -64,7 +64,7 @@ def test_dequant_nvfp4_every_nibble_every_scale(qh):
 
 def test_dequant_nvfp4_full_head_sampled(qh):
     wp, bs, g, wpd, bsd = nvfp4_head()
-    cfg = synth.CONFIGS[4]
+    cfg = synth.CONFIGS[synth.NVFP4_Q6K_129280X7168]
     log(f"[case] dequant nvfp4 full head {cfg.vocab}x{cfg.hidden}")
     out = qh.dequant_nvfp4_bf16(wpd, bsd, g)
     torch.cuda.synchronize()
@@ -102,7 +102,7 @@ def test_dequant_e8m0_rejects_uneven_groups(qh):
 # ------------------------------------------------- weight quantizers
 
 def _weights_with_edges(rows, hidden, seed):
-    wf = synth.weight_rows_f32(4, seed, seed + rows, hidden=hidden)
+    wf = synth.weight_rows_f32(synth.NVFP4_Q6K_129280X7168, seed, seed + rows, hidden=hidden)
     wf[1] = 0.0
     wf[2, :256] = 1e-9      # Q6_K: d underflows binary16 to 0
     wf[3, :256] *= 1e-3     # Q6_K: d is a binary16 subnormal
@@ -137,12 +137,12 @@ def test_quantize_q6k_rows_bit_exact(qh, rows, hidden):
 def test_quantize_full_heads_bit_exact(qh):
     """The 129280 x 7168 heads quantized on the GPU in one launch each match
     the oracle's chunked preparation byte for byte."""
-    cfg = synth.CONFIGS[4]
+    cfg = synth.CONFIGS[synth.NVFP4_Q6K_129280X7168]
     wp, bs, g, _, _ = nvfp4_head()
     blocks, _ = q6k_head()
     log(f"[case] quantize full heads {cfg.vocab}x{cfg.hidden}")
     wf = torch.empty((cfg.vocab, cfg.hidden), dtype=torch.float32, device=DEV)
-    for lo, hi, chunk in synth.iter_weight_chunks(4):
+    for lo, hi, chunk in synth.iter_weight_chunks(synth.NVFP4_Q6K_129280X7168):
         wf[lo:hi].copy_(torch.from_numpy(chunk))
     gwp, gbs = qh.quantize_nvfp4_rows(wf, g)
     gbl = qh.quantize_q6k_rows(wf)

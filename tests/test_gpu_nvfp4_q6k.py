@@ -64,7 +64,7 @@ def test_nvfp4_exact_dyadic_bit_exact(qh):
     assert np.array_equal(host_bits(out), oracle.bf16_rne_array(ref))
 
 
-def _nvfp4_small(V, H, cfg=4):
+def _nvfp4_small(V, H, cfg=synth.NVFP4_Q6K_129280X7168):
     wf = synth.weight_rows_f32(cfg, 0, V, vocab=V, hidden=H)
     g = oracle.nvfp4_global(float(np.abs(wf).max()))
     wp, bs = oracle.prep_nvfp4_rows(wf, g)
@@ -76,7 +76,7 @@ def test_nvfp4_edge_shapes(qh):
                        (4096, 64, 9)]:
         log(f"[case] nvfp4 edge V={V} H={H} rows={rows}")
         wp, bs, g = _nvfp4_small(V, H)
-        x = synth.activations_bf16(4, rows, hidden=H, max_rows=rows)
+        x = synth.activations_bf16(synth.NVFP4_Q6K_129280X7168, rows, hidden=H, max_rows=rows)
         out = qh.nvfp4(dev_u8(wp), dev_u8(bs), dev_bf16(x), g)
         torch.cuda.synchronize()
         ref, ad = oracle.nvfp4_ref(wp, bs, g, x)
@@ -85,27 +85,27 @@ def test_nvfp4_edge_shapes(qh):
 
 def test_nvfp4_zero_global_scale(qh):
     wp, bs, _ = _nvfp4_small(64, 256)
-    x = synth.activations_bf16(4, 2, hidden=256, max_rows=2)
+    x = synth.activations_bf16(synth.NVFP4_Q6K_129280X7168, 2, hidden=256, max_rows=2)
     out = host_bits(qh.nvfp4(dev_u8(wp), dev_u8(bs), dev_bf16(x), 0.0))
     assert (bf16_bits_to_f64(out) == 0).all()
 
 
-def test_nvfp4_cfg4_full_head(qh):
+def test_nvfp4_129280x7168_full_head(qh):
     """The 129280 x 7168 head at every row count 1..16 (one weight pass each:
     8192-wide tiles up to 8 rows, 4096-wide above) and a 40-row call
     (16 + 16 + 8); sampled logits within the bound, row-invariant bits."""
     wp, bs, g, wpd, bsd = nvfp4_head()
-    cfg = synth.CONFIGS[4]
-    x = synth.activations_bf16(4, 40, max_rows=40)
+    cfg = synth.CONFIGS[synth.NVFP4_Q6K_129280X7168]
+    x = synth.activations_bf16(synth.NVFP4_Q6K_129280X7168, 40, max_rows=40)
     vidx = sample_vidx(cfg.vocab, 1500, 4)
     ref, ad = oracle.nvfp4_ref(wp, bs, g, x, vidx)
     outs = {}
     for R in list(range(1, 17)) + [40]:
-        log(f"[case] nvfp4 cfg4 R={R}")
+        log(f"[case] nvfp4 129280x7168 R={R}")
         out = qh.nvfp4(wpd, bsd, dev_bf16(x[:R]), g)
         torch.cuda.synchronize()
         outs[R] = host_bits(out)
-        assert_within_bound(outs[R][:, vidx], ref[:R], ad[:R], f"nvfp4 cfg4 R={R}")
+        assert_within_bound(outs[R][:, vidx], ref[:R], ad[:R], f"nvfp4 129280x7168 R={R}")
     for R in outs:
         assert np.array_equal(outs[R], outs[40][:R]), f"row invariance R={R}"
 
@@ -116,7 +116,7 @@ def test_nvfp4_row_invariance_across_tile_widths(qh, H):
     8192-wide (<= 8 rows) and 4096-wide (9..16 rows) tiles."""
     V = 700
     wp, bs, g = _nvfp4_small(V, H)
-    x = synth.activations_bf16(4, 16, hidden=H, max_rows=16)
+    x = synth.activations_bf16(synth.NVFP4_Q6K_129280X7168, 16, hidden=H, max_rows=16)
     ref, ad = oracle.nvfp4_ref(wp, bs, g, x)
     wpd, bsd = dev_u8(wp), dev_u8(bs)
     outs = {}
@@ -132,7 +132,7 @@ def test_nvfp4_row_invariance_across_tile_widths(qh, H):
 
 def test_quant_q8_1_bit_exact(qh):
     H, rows = 7168, 19
-    x = synth.activations_bf16(4, rows, hidden=H, max_rows=rows)
+    x = synth.activations_bf16(synth.NVFP4_Q6K_129280X7168, rows, hidden=H, max_rows=rows)
     x[0, :64] = 0                        # two all-zero blocks
     x[1, :32] = 0x8000                   # a block of negative zeros
     ties = np.zeros(32, dtype=np.float32)
@@ -147,7 +147,7 @@ def test_quant_q8_1_bit_exact(qh):
 
 # ------------------------------------------------------------------- Q6_K
 
-def _q6k_small(V, H, cfg=4):
+def _q6k_small(V, H, cfg=synth.NVFP4_Q6K_129280X7168):
     wf = synth.weight_rows_f32(cfg, 0, V, vocab=V, hidden=H)
     return oracle.prep_q6k_rows(wf)
 
@@ -185,7 +185,7 @@ def test_q6k_edge_shapes_and_alignment(qh):
     for V, H, rows in [(1, 256, 1), (333, 768, 8), (70, 8448, 3), (1001, 1280, 11)]:
         log(f"[case] q6k edge V={V} H={H} rows={rows}")
         blocks = _q6k_small(V, H)
-        x = synth.activations_bf16(4, rows, hidden=H, max_rows=rows)
+        x = synth.activations_bf16(synth.NVFP4_Q6K_129280X7168, rows, hidden=H, max_rows=rows)
         q8 = oracle.quant_q8_1(x)
         ref, ad = oracle.q6k_ref(blocks, q8, H)
         out = qh.q6k(dev_u8(blocks), dev_bf16(x))
@@ -200,20 +200,20 @@ def test_q6k_edge_shapes_and_alignment(qh):
         assert np.array_equal(host_bits(out2), host_bits(out))
 
 
-def test_q6k_cfg4_full_head(qh):
+def test_q6k_129280x7168_full_head(qh):
     blocks, bd = q6k_head()
-    cfg = synth.CONFIGS[4]
-    x = synth.activations_bf16(4, 8)
+    cfg = synth.CONFIGS[synth.NVFP4_Q6K_129280X7168]
+    x = synth.activations_bf16(synth.NVFP4_Q6K_129280X7168, 8)
     q8 = oracle.quant_q8_1(x)
     vidx = sample_vidx(cfg.vocab, 1000, 5)
     ref, ad = oracle.q6k_ref(blocks, q8, cfg.hidden, vidx)
     ws = torch.empty((qh.q6k_workspace_bytes(cfg.hidden),), dtype=torch.uint8, device=DEV)
     outs = {}
     for R in range(1, 9):
-        log(f"[case] q6k cfg4 R={R}")
+        log(f"[case] q6k 129280x7168 R={R}")
         out = qh.q6k(bd, dev_bf16(x[:R]), workspace=ws)
         torch.cuda.synchronize()
         outs[R] = host_bits(out)
-        assert_within_bound(outs[R][:, vidx], ref[:R], ad[:R], f"q6k cfg4 R={R}")
+        assert_within_bound(outs[R][:, vidx], ref[:R], ad[:R], f"q6k 129280x7168 R={R}")
     for R in range(1, 9):
         assert np.array_equal(outs[R], outs[8][:R]), f"row invariance R={R}"

@@ -30,7 +30,7 @@ def _bits(v):
 
 def _gate_up(rows, hidden, ld, seed):
     """Seeded gate/up [rows, ld] with edge rows planted in the first rows."""
-    g, u = synth.gate_up_bf16(5, rows, hidden=ld, max_rows=rows)
+    g, u = synth.gate_up_bf16(synth.SILU_DOWN_7168X18432, rows, hidden=ld, max_rows=rows)
     g, u = g.copy(), u.copy()
     rng = np.random.Generator(np.random.PCG64(seed))
     if rows > 1:
@@ -98,7 +98,7 @@ def test_quant_act_silu_bit_exact(qh, rows, hidden, ld):
 
 
 def _fp8_weights(V, H, seed):
-    wf = synth.weight_rows_f32(5, 0, V, vocab=V, hidden=H)
+    wf = synth.weight_rows_f32(synth.SILU_DOWN_7168X18432, 0, V, vocab=V, hidden=H)
     return oracle.prep_fp8_rows(wf)
 
 
@@ -128,9 +128,9 @@ def test_w8a8_silu_logits_and_row_invariance(qh):
 def test_w8a8_silu_full_size(qh):
     """The 7168 x 18432 down projection at rows 1, 16, 128 and 130 (a 128-row
     chunk plus 2); sampled outputs within the bound, row-invariant bits."""
-    w, s, wd, sd = fp8_head(5)
-    cfg = synth.CONFIGS[5]
-    g, u = synth.gate_up_bf16(5, 130)
+    w, s, wd, sd = fp8_head(synth.SILU_DOWN_7168X18432)
+    cfg = synth.CONFIGS[synth.SILU_DOWN_7168X18432]
+    g, u = synth.gate_up_bf16(synth.SILU_DOWN_7168X18432, 130)
     xq, sa, amb = oracle.quant_act_silu_e4m3(g, u)
     assert amb == 0
     vidx = sample_vidx(cfg.vocab, 700, 5)
@@ -138,11 +138,11 @@ def test_w8a8_silu_full_size(qh):
     ws = qh.w8a8_workspace(cfg.hidden, DEV)
     outs = {}
     for R in cfg.rows:
-        log(f"[case] w8a8_silu cfg5 R={R}")
+        log(f"[case] w8a8_silu 7168x18432 R={R}")
         out = qh.w8a8_silu(wd, sd, dev_bf16(g[:R]), dev_bf16(u[:R]), workspace=ws)
         torch.cuda.synchronize()
         outs[R] = host_bits(out)
-        assert_within_bound(outs[R][:, vidx], ref[:R], ad[:R], f"cfg5 R={R}")
+        assert_within_bound(outs[R][:, vidx], ref[:R], ad[:R], f"7168x18432 R={R}")
     for R in cfg.rows:
         assert np.array_equal(outs[R], outs[130][:R]), f"row invariance R={R}"
 

@@ -205,7 +205,7 @@ def test_quant_act_e4m3_worked_row():
 
 
 def test_quant_act_e4m3_properties():
-    xf = synth.activations_f32(1, 16, max_rows=16)
+    xf = synth.activations_f32(synth.FP8_32000X4096, 16, max_rows=16)
     x = synth.to_bf16_bits(xf)
     xq, sa = oracle.quant_act_e4m3(x)
     xv = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).float().numpy()
@@ -253,7 +253,7 @@ def test_quant_q8_1_worked_ties():
 
 
 def test_quant_q8_1_properties():
-    x = synth.activations_bf16(4, 3, hidden=256, max_rows=3)
+    x = synth.activations_bf16(synth.NVFP4_Q6K_129280X7168, 3, hidden=256, max_rows=3)
     q8 = oracle.quant_q8_1(x).reshape(3, 8, 36)
     xv = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).double().numpy().reshape(3, 8, 32)
     for r in range(3):
@@ -328,9 +328,9 @@ def _bf16_np(x):
 
 
 def test_fp8_ref_matches_numpy_matmul():
-    wf = synth.weight_rows_f32(0, 0, 512)
+    wf = synth.weight_rows_f32(synth.FP8_8192X1024, 0, 512)
     w, s = oracle.prep_fp8_rows(wf)
-    x = synth.activations_bf16(0, 3, max_rows=3)
+    x = synth.activations_bf16(synth.FP8_8192X1024, 3, max_rows=3)
     ref, ad = oracle.fp8_rowscale_ref(w, s, x)
     W = _dequant_fp8_np(w, s)
     X = _bf16_np(x)
@@ -377,9 +377,9 @@ def test_w8a8_ref_is_exact():
 
 
 def test_w8a8_ref_matches_numpy_on_quantized_rows():
-    wf = synth.weight_rows_f32(3, 0, 256, hidden=512)
+    wf = synth.weight_rows_f32(synth.W8A8_129280X7168, 0, 256, hidden=512)
     w, sw = oracle.prep_fp8_rows(wf)
-    x = synth.activations_bf16(3, 5, hidden=512, max_rows=5)
+    x = synth.activations_bf16(synth.W8A8_129280X7168, 5, hidden=512, max_rows=5)
     xq, sa = oracle.quant_act_e4m3(x)
     ref, _ = oracle.w8a8_ref(w, sw, xq, sa)
     T = _torch_e4m3_decode_all()
@@ -390,10 +390,10 @@ def test_w8a8_ref_matches_numpy_on_quantized_rows():
 
 def test_nvfp4_ref_matches_numpy_matmul():
     V, H = 300, 512
-    wf = synth.weight_rows_f32(4, 0, V, hidden=H)
+    wf = synth.weight_rows_f32(synth.NVFP4_Q6K_129280X7168, 0, V, hidden=H)
     g = oracle.nvfp4_global(float(np.abs(wf).max()))
     wp, bs = oracle.prep_nvfp4_rows(wf, g)
-    x = synth.activations_bf16(4, 4, hidden=H, max_rows=4)
+    x = synth.activations_bf16(synth.NVFP4_Q6K_129280X7168, 4, hidden=H, max_rows=4)
     ref, ad = oracle.nvfp4_ref(wp, bs, g, x)
     table = np.array([float(v) for _, v in _rows("e2m1_table.txt")])
     nib = np.empty((V, H), dtype=np.uint8)
@@ -408,9 +408,9 @@ def test_nvfp4_ref_matches_numpy_matmul():
 
 def test_q6k_ref_matches_numpy_matmul():
     V, H = 64, 512
-    wf = synth.weight_rows_f32(4, 0, V, hidden=H)
+    wf = synth.weight_rows_f32(synth.NVFP4_Q6K_129280X7168, 0, V, hidden=H)
     blocks = oracle.prep_q6k_rows(wf)
-    x = synth.activations_bf16(4, 3, hidden=H, max_rows=3)
+    x = synth.activations_bf16(synth.NVFP4_Q6K_129280X7168, 3, hidden=H, max_rows=3)
     q8 = oracle.quant_q8_1(x)
     ref, _ = oracle.q6k_ref(blocks, q8, H)
     W = np.stack([np.concatenate([oracle.q6k_decode_block(blocks[v, b * 210:(b + 1) * 210])
@@ -425,7 +425,7 @@ def test_q6k_ref_matches_numpy_matmul():
 
 
 def test_prep_fp8_rows_properties():
-    wf = synth.weight_rows_f32(2, 0, 64, hidden=1024)
+    wf = synth.weight_rows_f32(synth.FP8_155136X8192, 0, 64, hidden=1024)
     wf[3] = 0
     codes, s = oracle.prep_fp8_rows(wf)
     assert s[3] == 0 and not codes[3].any()
@@ -439,9 +439,9 @@ def test_prep_fp8_rows_properties():
 
 def test_oracle_rows_independent_of_row_count():
     # a row's reference does not depend on which other rows are present
-    wf = synth.weight_rows_f32(0, 0, 128)
+    wf = synth.weight_rows_f32(synth.FP8_8192X1024, 0, 128)
     w, s = oracle.prep_fp8_rows(wf)
-    x = synth.activations_bf16(0, 5, max_rows=5)
+    x = synth.activations_bf16(synth.FP8_8192X1024, 5, max_rows=5)
     full, _ = oracle.fp8_rowscale_ref(w, s, x)
     for r in range(5):
         one, _ = oracle.fp8_rowscale_ref(w, s, x[r:r + 1])
@@ -449,13 +449,13 @@ def test_oracle_rows_independent_of_row_count():
 
 
 def test_synth_row_ranges_are_stable():
-    a = synth.weight_rows_f32(1, 1000, 1100)
-    b = synth.weight_rows_f32(1, 0, 2048)[1000:1100]
+    a = synth.weight_rows_f32(synth.FP8_32000X4096, 1000, 1100)
+    b = synth.weight_rows_f32(synth.FP8_32000X4096, 0, 2048)[1000:1100]
     assert np.array_equal(a, b)
-    x4 = synth.activations_f32(1, 4)
-    x40 = synth.activations_f32(1, 40)
+    x4 = synth.activations_f32(synth.FP8_32000X4096, 4)
+    x40 = synth.activations_f32(synth.FP8_32000X4096, 40)
     assert np.array_equal(x4, x40[:4])
-    cols = synth.outlier_columns(1, 4096, 41)
+    cols = synth.outlier_columns(synth.FP8_32000X4096, 4096, 41)
     assert len(cols) == 41
 
 
@@ -556,7 +556,7 @@ def test_dequant_e8m0_group_boundaries():
 # ------------------------------------------- NVFP4 / Q6_K weight preparation
 
 def test_prep_nvfp4_rows_nearest_codes():
-    wf = synth.weight_rows_f32(4, 0, 24, hidden=512)
+    wf = synth.weight_rows_f32(synth.NVFP4_Q6K_129280X7168, 0, 24, hidden=512)
     wf[5] = 0
     g = oracle.nvfp4_global(float(np.abs(wf).max()))
     assert g == np.float32(np.abs(wf).max()) / np.float32(2688)
@@ -581,7 +581,7 @@ def test_prep_nvfp4_rows_nearest_codes():
 
 
 def test_prep_q6k_rows_nearest_levels():
-    wf = synth.weight_rows_f32(4, 0, 6, hidden=512)
+    wf = synth.weight_rows_f32(synth.NVFP4_Q6K_129280X7168, 0, 6, hidden=512)
     wf[2, :256] = 0
     blocks = oracle.prep_q6k_rows(wf)
     sb = blocks.reshape(6, 2, 210)
