@@ -200,6 +200,18 @@ def test_dequant_validation(qh):
     assert g(None, None, 0, 3, None, None) == 0
 
 
+def test_header_is_plain_c(qh, tmp_path):
+    """A C99 program includes include/qhead.h (-pedantic -Werror), links the
+    library and calls its host-side entry points."""
+    exe = tmp_path / "c_abi_smoke"
+    libdir = os.path.dirname(qh.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c_abi_smoke.c"),
+                    "-L", libdir, "-lqhead", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    run = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert run.returncode == 0, run.stdout + run.stderr
+
+
 def test_binding_rejects_host_tensors(qh):
     import torch
 
