@@ -155,11 +155,52 @@ fp8_gemv_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
                     e4m3x4_to_bf16(cur[t].z, wb[t][4], wb[t][5]);
                     e4m3x4_to_bf16(cur[t].w, wb[t][6], wb[t][7]);
                 }
+                const uint4* xrow = xs + s * 128 + lane;
+                if constexpr (R >= 4) {
+                    // Rows in groups of G: for each k pair p, the G * T
+                    // accumulators of a group take their dot2 one after the
+                    // other, so a chain's next dot2 is G * T instructions
+                    // away (the VALU issues near its peak only with many
+                    // independent chains). Each accumulator still sums p in
+                    // order, so the arithmetic is the same for every R. The
+                    // next group's activations are read while this one runs.
+                    constexpr int G = 4;
+                    uint32_t xg[2][G][8];
+                    auto read_group = [&](int rg, uint32_t (&dst)[G][8]) {
+#pragma unroll
+                        for (int g = 0; g < G; ++g) {
+                            if (rg + g < R) {
+                                const uint4 xa = xrow[(rg + g) * kVecPerTileRow];
+                                const uint4 xb = xrow[(rg + g) * kVecPerTileRow + 64];
+                                dst[g][0] = xa.x; dst[g][1] = xa.y; dst[g][2] = xa.z;
+                                dst[g][3] = xa.w; dst[g][4] = xb.x; dst[g][5] = xb.y;
+                                dst[g][6] = xb.z; dst[g][7] = xb.w;
+                            }
+                        }
+                    };
+                    read_group(0, xg[0]);
+#pragma unroll
+                    for (int rg = 0; rg < R; rg += G) {
+                        if (rg + G < R) read_group(rg + G, xg[((rg / G) + 1) & 1]);
+                        const int cb = (rg / G) & 1;
+#pragma unroll
+                        for (int p = 0; p < 8; ++p) {
+#pragma unroll
+                            for (int g = 0; g < G; ++g) {
+                                if (rg + g < R) {
+#pragma unroll
+                                    for (int t = 0; t < T; ++t)
+                                        acc[(rg + g) * T + t] =
+                                            dot2_bf16(xg[cb][g][p], wb[t][p], acc[(rg + g) * T + t]);
+                                }
+                            }
+                        }
+                    }
+                } else {
                 // Activation rows through a ring of LA + 1 buffers: the
                 // reads of row r + LA are issued before row r is computed.
                 constexpr int LA = R < 2 ? R : 2;
                 constexpr int NBUF = LA + 1;
-                const uint4* xrow = xs + s * 128 + lane;
                 uint4 xr[NBUF][2];
 #pragma unroll
                 for (int r = 0; r < LA; ++r) {
@@ -181,6 +222,7 @@ fp8_gemv_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
                         for (int p = 0; p < 8; ++p) a = dot2_bf16(xv[p], wb[t][p], a);
                         acc[r * T + t] = a;
                     }
+                }
                 }
                 if (s + 1 == nseg) {
                     wave_reduce_scatter<NP>(acc, lane);
