@@ -17,6 +17,12 @@
  *                       quantized to q8_1 blocks (qhead_quant_q8_1), <= 8
  *                       rows per pass.
  *
+ * Next to the head: qhead_w8a8_silu, the W8A8 down projection of a SiLU FFN
+ * (bf16(silu(gate) * up) quantized per row, then the W8A8 GEMV); the
+ * load-time conversions qhead_dequant_nvfp4_bf16 and
+ * qhead_dequant_fp4_e8m0_bf16; and device-side weight preparation
+ * (qhead_quantize_fp8_rows / _nvfp4_rows / _q6k_rows).
+ *
  * Conventions (all entry points):
  *  - Pointers are device memory owned by the caller, unless stated. The
  *    library allocates nothing and keeps no state between calls apart from a
@@ -40,8 +46,10 @@
  *
  * Numerical contract (checked against a binary64 CPU oracle): with ref the
  * exact dot product of the dequantized operands times the scales,
- *   |out - ref| <= 2^-7 |ref| + 1e-4 sum_k |x_k w_k|,
- * and the activation quantizers' bytes are exactly those of the oracle.
+ *   |out - ref| <= 2^-7 |ref| + 1e-4 sum_k |x_k w_k|
+ * (plus 2^-134, half of BF16's subnormal spacing, for logits BF16 can only
+ * hold as subnormals), and the quantizers' and converters' bytes are
+ * exactly those of the oracle.
  *
  * Passages cited below are items of the pages "lm_head_fp8_rows.rs",
  * "w8a8_layer.rs", "fp8_lut.rs", "lm_head_q6k.rs" and "w4a16_gemv_tiers.rs".
