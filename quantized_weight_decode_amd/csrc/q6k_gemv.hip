@@ -36,11 +36,19 @@ constexpr int kQSbPerTile = kQTileK / 256;
 
 // LDS per workgroup, sized by the row count so that small R leaves room for
 // several workgroups per CU.
+// The q8 values of a super-block (256 k) take 256 + 16 bytes and its 16
+// sub-block offsets 16 + 1 words: the super-blocks one half wave reads at
+// once then start in different LDS banks.
+constexpr int kQPadSb = 256 + 16;
+constexpr int kOffPadSb = 16 + 1;
+__device__ __forceinline__ int q_pos(int k) { return (k >> 8) * kQPadSb + (k & 255); }
+__device__ __forceinline__ int off_pos(int k) { return (k >> 8) * kOffPadSb + ((k & 255) >> 4); }
+
 template <int R>
-struct Q6Lds {
-    int8_t q[R][kQTileK];               // q8 values [row][k]
-    float d8[R][kQTileK / 32];          // fp16 d of each q8 block, as f32
-    int32_t off[R][kQTileK / 16];       // -32 * sum of q8 over each 16-value sub-block
+struct alignas(16) Q6Lds {
+    int8_t q[R][kQSbPerTile * kQPadSb];     // q8 values [row][k], padded per super-block
+    float d8[R][kQTileK / 32];              // fp16 d of each q8 block, as f32
+    int32_t off[R][kQSbPerTile * kOffPadSb];  // -32 * sum of q8 per 16-value sub-block, padded
 };
 
 template <int R, int NTHREADS>
@@ -61,13 +69,13 @@ __device__ __forceinline__ void q6_stage_tile(Q6Lds<R>& L, const uint8_t* q8, in
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const uint32_t w = src[1 + i];
-            *reinterpret_cast<uint32_t*>(&L.q[r][j * 32 + 4 * i]) = w;
+            *reinterpret_cast<uint32_t*>(&L.q[r][q_pos(j * 32 + 4 * i)]) = w;
             const int sum4 = __builtin_amdgcn_sdot4((int)w, 0x01010101, 0, false);
             if (i < 4) s0 += sum4;
             else s1 += sum4;
         }
-        L.off[r][2 * j] = -32 * s0;
-        L.off[r][2 * j + 1] = -32 * s1;
+        L.off[r][off_pos(j * 32)] = -32 * s0;
+        L.off[r][off_pos(j * 32 + 16)] = -32 * s1;
     }
 }
 
@@ -207,8 +215,8 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                 const int kk = min(sbt, kQSbPerTile - 1) * 256 + 16 * t16;  // k within the tile
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const uint4 xq = *reinterpret_cast<const uint4*>(&L.q[r][kk]);
-                    const int off = L.off[r][kk >> 4];
+                    const uint4 xq = *reinterpret_cast<const uint4*>(&L.q[r][q_pos(kk)]);
+                    const int off = L.off[r][off_pos(kk)];
                     const float d8 = valid ? L.d8[r][kk >> 5] : 0.0f;
 #pragma unroll
                     for (int t = 0; t < T; ++t) {
