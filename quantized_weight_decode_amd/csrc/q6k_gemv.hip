@@ -115,6 +115,21 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     const int qh_off = 128 + 32 * n + 16 * h;
     const int lo_shift = (c >= 2) ? 4 : 0;
     const int hi_shift = 2 * c;
+    // Byte offsets within a staged item of this lane's fields (before the
+    // item's misalignment), and the bit added to 8 x the byte address of the
+    // 32-bit window each field is funnel-shifted from: the low nibbles of ql
+    // land in bits 0-3 of each byte, the 2-bit qh fields in bits 4-5. When
+    // the qh field sits below bit 4 the window starts one byte earlier.
+    // The offsets count from the block's first staging buffer and include
+    // this wave's buffers (a multiple of 4 bytes).
+    const int qh_back = hi_shift < 4 ? 1 : 0;
+    const int p_sb = wave * (T * kWave * 16) + sbi * kQ6KBlockBytes;
+    const int p_ql = p_sb + ql_off;
+    const int p_qh = p_sb + qh_off - qh_back;
+    const int b_qh = 8 * qh_back + hi_shift - 4;
+    const int p_sc = p_sb + 192 + t16;
+    const int p_d = p_sb + 208;
+    const uint8_t* const wb = reinterpret_cast<const uint8_t*>(&WB[0][0][0]);
 
     const int my_idx = lane >> (6 - M);
     const int my_r = my_idx / T;
@@ -188,26 +203,29 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                 float wsc[T];
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
-                    const uintptr_t a = reinterpret_cast<uintptr_t>(item_ptr(bi, s, t));
-                    const int rel = (int)(a & 15) + sbi * kQ6KBlockBytes;  // LDS byte offset
-                    const uint32_t sh = (uint32_t)(rel & 3);
-                    const uint8_t* lb = reinterpret_cast<const uint8_t*>(&WB[wave][t][0]);
-                    const uint32_t* lw = reinterpret_cast<const uint32_t*>(lb + (rel & ~3));
+                    // item start within row t's staging buffer (wave-uniform)
+                    const int st = (int)(reinterpret_cast<uintptr_t>(item_ptr(bi, s, t)) & 15) +
+                                   t * kWave * 16;
+                    const int aql = st + p_ql, aqh = st + p_qh;
+                    const uint32_t* wl = reinterpret_cast<const uint32_t*>(wb + (aql & ~3));
+                    const uint32_t* wh = reinterpret_cast<const uint32_t*>(wb + (aqh & ~3));
+                    // alignbit takes its shift modulo 32
+                    const uint32_t shl = (uint32_t)(8 * aql + lo_shift);
+                    const uint32_t shh = (uint32_t)(8 * aqh + b_qh);
                     uint32_t qlw[5], qhw[5];
 #pragma unroll
                     for (int i = 0; i < 5; ++i) {
-                        qlw[i] = lw[ql_off / 4 + i];
-                        qhw[i] = lw[qh_off / 4 + i];
+                        qlw[i] = wl[i];
+                        qhw[i] = wh[i];
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const uint32_t ql = __builtin_amdgcn_alignbyte(qlw[i + 1], qlw[i], sh);
-                        const uint32_t qh = __builtin_amdgcn_alignbyte(qhw[i + 1], qhw[i], sh);
-                        qw[t][i] = ((ql >> lo_shift) & 0x0F0F0F0Fu) |
-                                   (((qh >> hi_shift) & 0x03030303u) << 4);
+                        const uint32_t lo = __builtin_amdgcn_alignbit(qlw[i + 1], qlw[i], shl);
+                        const uint32_t hi = __builtin_amdgcn_alignbit(qhw[i + 1], qhw[i], shh);
+                        qw[t][i] = (lo & 0x0F0F0F0Fu) | (hi & 0x30303030u);
                     }
-                    const int sc = (int)(int8_t)lb[rel + 192 + t16];
-                    const uint16_t dbits = *reinterpret_cast<const uint16_t*>(lb + rel + 208);
+                    const int sc = reinterpret_cast<const int8_t*>(wb)[st + p_sc];
+                    const uint16_t dbits = *reinterpret_cast<const uint16_t*>(wb + st + p_d);
                     // d * sc is exact in FP32 (11-bit times 8-bit significands)
                     const float d = (float)__builtin_bit_cast(_Float16, dbits);
                     wsc[t] = valid ? d * (float)sc : 0.0f;
