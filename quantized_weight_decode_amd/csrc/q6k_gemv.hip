@@ -130,6 +130,22 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     const int p_sc = p_sb + 192 + t16;
     const int p_d = p_sb + 208;
     const uint8_t* const wb = reinterpret_cast<const uint8_t*>(&WB[0][0][0]);
+    // An item's first byte is 2-byte aligned, and its position mod 4 in the
+    // staging buffer depends only on the parity of its vocab row: items start
+    // at multiples of 840 bytes within a row, rows are hidden/256 x 210 bytes
+    // apart and bands start at even rows. So the 32-bit window of each field
+    // and its funnel shift take one of two lane values, for even and odd rows
+    // (a row re-read past the vocab tail may take the wrong one: its sums are
+    // never stored).
+    static_assert(T % 2 == 0, "bands must start at even rows");
+    const int c_even = (int)(reinterpret_cast<uintptr_t>(blocks) & 3);
+    const int c_odd = (c_even + 2 * (nsb & 1)) & 3;
+    const int wl_even = (p_ql + c_even) & ~3, wl_odd = (p_ql + c_odd) & ~3;
+    const int wh_even = (p_qh + c_even) & ~3, wh_odd = (p_qh + c_odd) & ~3;
+    const uint32_t sl_even = 8 * ((p_ql + c_even) & 3) + lo_shift;
+    const uint32_t sl_odd = 8 * ((p_ql + c_odd) & 3) + lo_shift;
+    const uint32_t sh_even = 8 * ((p_qh + c_even) & 3) + b_qh;
+    const uint32_t sh_odd = 8 * ((p_qh + c_odd) & 3) + b_qh;
 
     const int my_idx = lane >> (6 - M);
     const int my_r = my_idx / T;
@@ -203,15 +219,18 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                 float wsc[T];
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
-                    // item start within row t's staging buffer (wave-uniform)
+                    // item start within row t's staging buffer, and that
+                    // rounded down to a word (wave-uniform)
                     const int st = (int)(reinterpret_cast<uintptr_t>(item_ptr(bi, s, t)) & 15) +
                                    t * kWave * 16;
-                    const int aql = st + p_ql, aqh = st + p_qh;
-                    const uint32_t* wl = reinterpret_cast<const uint32_t*>(wb + (aql & ~3));
-                    const uint32_t* wh = reinterpret_cast<const uint32_t*>(wb + (aqh & ~3));
+                    const int sw = st & ~3;
+                    const uint32_t* wl =
+                        reinterpret_cast<const uint32_t*>(wb + sw + ((t & 1) ? wl_odd : wl_even));
+                    const uint32_t* wh =
+                        reinterpret_cast<const uint32_t*>(wb + sw + ((t & 1) ? wh_odd : wh_even));
                     // alignbit takes its shift modulo 32
-                    const uint32_t shl = (uint32_t)(8 * aql + lo_shift);
-                    const uint32_t shh = (uint32_t)(8 * aqh + b_qh);
+                    const uint32_t shl = (t & 1) ? sl_odd : sl_even;
+                    const uint32_t shh = (t & 1) ? sh_odd : sh_even;
                     uint32_t qlw[5], qhw[5];
 #pragma unroll
                     for (int i = 0; i < 5; ++i) {
@@ -224,7 +243,11 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                         const uint32_t hi = __builtin_amdgcn_alignbit(qhw[i + 1], qhw[i], shh);
                         qw[t][i] = (lo & 0x0F0F0F0Fu) | (hi & 0x30303030u);
                     }
-                    const int sc = reinterpret_cast<const int8_t*>(wb)[st + p_sc];
+                    int sc = reinterpret_cast<const int8_t*>(wb)[st + p_sc];
+                    // keep sc a 32-bit value: a sign-extending byte load and
+                    // one convert (otherwise the convert is narrowed to 16
+                    // bits and costs an extra bit-field extract)
+                    asm("" : "+v"(sc));
                     const uint16_t dbits = *reinterpret_cast<const uint16_t*>(wb + st + p_d);
                     // d * sc is exact in FP32 (11-bit times 8-bit significands)
                     const float d = (float)__builtin_bit_cast(_Float16, dbits);
