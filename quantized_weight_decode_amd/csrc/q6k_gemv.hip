@@ -289,11 +289,17 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                 if (nitems > 1) { if (++s1 == nseg) { s1 = 0; ++bi1; } }
                 issue(bi1, s1, gB);
             }
+            // The loop body always runs both steps: a conditional second
+            // step would let the loop back edge carry loads into gA still in
+            // flight, and the wait counters at the loop head would then
+            // drain every load (including item it + 1's) before issuing.
+            int it = 0;
 #pragma unroll 1
-            for (int it = 0; it < nitems; it += 2) {
+            for (; it + 1 < nitems; it += 2) {
                 step(it, gA, gB);
-                if (it + 1 < nitems) step(it + 1, gB, gA);
+                step(it + 1, gB, gA);
             }
+            if (it < nitems) step(it, gA, gB);
         }
 
 #pragma unroll
