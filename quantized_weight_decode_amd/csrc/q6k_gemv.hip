@@ -261,7 +261,10 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                     const float d8 = valid ? L.d8[r][kk >> 5] : 0.0f;
 #pragma unroll
                     for (int t = 0; t < T; ++t) {
-                        int is = __builtin_amdgcn_sdot4((int)qw[t][0], (int)xq.x, off, false);
+                        // The clamp (saturation) never acts: |is| < 2^18. It
+                        // selects the three-operand encoding, so the chain
+                        // starts from `off` without first copying it.
+                        int is = __builtin_amdgcn_sdot4((int)qw[t][0], (int)xq.x, off, true);
                         is = __builtin_amdgcn_sdot4((int)qw[t][1], (int)xq.y, is, false);
                         is = __builtin_amdgcn_sdot4((int)qw[t][2], (int)xq.z, is, false);
                         is = __builtin_amdgcn_sdot4((int)qw[t][3], (int)xq.w, is, false);
