@@ -90,10 +90,11 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     static_assert(NP <= 64 && R <= 8, "T*R must be <= 64, R <= 8");
     static_assert(kItemBytes + 15 <= 64 * 16, "an item must fit one 16-byte load per lane");
     __shared__ Q6Lds<R> L;
-    // wave-private weight staging: [wave][row t][1024 bytes]. One buffer is
-    // enough: a wave's LDS instructions execute in order, so the item written
-    // after the current item's reads never overtakes them.
-    __shared__ u32x4_t WB[WAVES][T][kWave];
+    // wave-private weight staging, two buffers: [wave][item parity][row t]
+    // [1024 bytes]. Item it + 1 is written into one buffer at the start of
+    // step it, while item it is read from the other, so a whole step
+    // separates each item's LDS write from its reads.
+    __shared__ u32x4_t WB[WAVES][2][T][kWave];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -123,7 +124,7 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     // The offsets count from the block's first staging buffer and include
     // this wave's buffers (a multiple of 4 bytes).
     const int qh_back = hi_shift < 4 ? 1 : 0;
-    const int p_sb = wave * (T * kWave * 16) + sbi * kQ6KBlockBytes;
+    const int p_sb = wave * (2 * T * kWave * 16) + sbi * kQ6KBlockBytes;
     const int p_ql = p_sb + ql_off;
     const int p_qh = p_sb + qh_off - qh_back;
     const int b_qh = 8 * qh_back + hi_shift - 4;
@@ -193,22 +194,24 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                     g[t] = *reinterpret_cast<const u32x4_t*>(p16 + 16 * ch);
                 }
             };
-            auto stage = [&](const u32x4_t (&g)[T]) {
+            auto stage = [&](const u32x4_t (&g)[T], int buf) {
 #pragma unroll
-                for (int t = 0; t < T; ++t) WB[wave][t][lane] = g[t];
+                for (int t = 0; t < T; ++t) WB[wave][buf][t][lane] = g[t];
             };
 
             float acc[NP];
             int bi = 0, s = 0;
-            // Item `it` is in LDS; item it + 1 is in flight in `gn`; `gf` is
-            // free and receives item it + 2.
-            auto step = [&](int it, u32x4_t (&gf)[T], const u32x4_t (&gn)[T]) {
+            // Item `it` is in LDS buffer `buf`; item it + 1 is in flight in
+            // `gn` and goes to the other buffer; `gf` is free and receives
+            // item it + 2. `buf` is it's parity (a constant at each call).
+            auto step = [&](int it, int buf, u32x4_t (&gf)[T], const u32x4_t (&gn)[T]) {
                 // (bi, s) of items it + 1 and it + 2, clamped to the last item
                 int bi1 = bi, s1 = s;
                 if (it + 1 < nitems) { if (++s1 == nseg) { s1 = 0; ++bi1; } }
                 int bi2 = bi1, s2 = s1;
                 if (it + 2 < nitems) { if (++s2 == nseg) { s2 = 0; ++bi2; } }
                 issue(bi2, s2, gf);
+                stage(gn, buf ^ 1);
                 if (s == 0) {
 #pragma unroll
                     for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
@@ -222,7 +225,7 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                     // item start within row t's staging buffer, and that
                     // rounded down to a word (wave-uniform)
                     const int st = (int)(reinterpret_cast<uintptr_t>(item_ptr(bi, s, t)) & 15) +
-                                   t * kWave * 16;
+                                   (buf * T + t) * kWave * 16;
                     const int sw = st & ~3;
                     const uint32_t* wl =
                         reinterpret_cast<const uint32_t*>(wb + sw + ((t & 1) ? wl_odd : wl_even));
@@ -271,8 +274,6 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                         acc[r * T + t] = __builtin_fmaf((float)is, wsc[t] * d8, acc[r * T + t]);
                     }
                 }
-                // item it + 1 replaces item it (after all of item it's reads)
-                stage(gn);
                 if (s + 1 == nseg) {
                     wave_reduce_scatter<NP>(acc, lane);
 #pragma unroll
@@ -287,7 +288,7 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
             u32x4_t gA[T], gB[T];
             if (nitems > 0) {
                 issue(0, 0, gA);
-                stage(gA);
+                stage(gA, 0);
                 int bi1 = 0, s1 = 0;
                 if (nitems > 1) { if (++s1 == nseg) { s1 = 0; ++bi1; } }
                 issue(bi1, s1, gB);
@@ -299,10 +300,10 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
             int it = 0;
 #pragma unroll 1
             for (; it + 1 < nitems; it += 2) {
-                step(it, gA, gB);
-                step(it + 1, gB, gA);
+                step(it, 0, gA, gB);
+                step(it + 1, 1, gB, gA);
             }
-            if (it < nitems) step(it, gA, gB);
+            if (it < nitems) step(it, 0, gA, gB);
         }
 
 #pragma unroll
