@@ -336,7 +336,7 @@ hipError_t run_q6k(const uint8_t* blocks, const uint8_t* q8, int R, int H, int V
     case RR:                            \
         return launch_q6k<RR, TT, WV, MB, BPC>(blocks, q8, H, V, out, dev, stream);
         QH_Q6_CASE(1, 4, 8, 12, 2)
-        QH_Q6_CASE(2, 2, 16, 12, 1)
+        QH_Q6_CASE(2, 2, 12, 8, 2)
         QH_Q6_CASE(3, 2, 16, 12, 1)
         QH_Q6_CASE(4, 2, 16, 12, 1)
         QH_Q6_CASE(5, 4, 8, 12, 1)
