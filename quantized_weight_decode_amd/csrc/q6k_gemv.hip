@@ -21,11 +21,14 @@
 // vocab rows per item. Those 840 bytes are fetched with one fully coalesced
 // 16-byte load per lane (the aligned 16-byte chunks that hold them; a chunk
 // holding at least one byte of the item never crosses a page) and written
-// to a wave-private LDS buffer; each lane then reads its fields from LDS as
-// aligned dwords and realigns them with v_alignbyte (super-blocks are only
-// 2-byte aligned). Two items are in flight in registers while one is being
-// computed from LDS. The -32 offset is folded into the integer dot: the
-// staging step stores -32 * sum(q8) per sub-block next to the q8 values.
+// to one of two wave-private LDS buffers; each lane then reads its fields
+// from LDS as aligned dwords and cuts four 6-bit codes at a time out of them
+// with v_alignbit funnel shifts (super-blocks are only 2-byte aligned; the
+// shift folds the misalignment and the field's bit position). While item it
+// is computed from one buffer, item it + 1 has been written to the other
+// and item it + 2 is in flight in registers. The -32 offset is folded into
+// the integer dot: the staging step stores -32 * sum(q8) per sub-block next
+// to the q8 values.
 #include "qhead_device.h"
 #include "qhead_internal.h"
 
