@@ -164,7 +164,7 @@ fp8_gemv_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
                     // independent chains). Each accumulator still sums p in
                     // order, so the arithmetic is the same for every R. The
                     // next group's activations are read while this one runs.
-                    constexpr int G = 4;
+                    constexpr int G = T >= 4 ? 4 : 2;  // 2-row bands: fewer live registers
                     uint32_t xg[2][G][8];
                     auto read_group = [&](int rg, uint32_t (&dst)[G][8]) {
 #pragma unroll
@@ -301,6 +301,28 @@ template <bool W8A8>
 static hipError_t dispatch_fp8(int R, const uint8_t* W, const float* wscale, const void* x,
                                const float* xscale, int H, int V, uint16_t* out,
                                const DeviceInfo& dev, hipStream_t stream) {
+    // Heads with few vocab rows (the SiLU down projection's 7168): with
+    // 4-row bands the 9..16-row shape gives a wave fewer than two bands and
+    // leaves waves idle; 2-row bands in 16-wave groups keep them busy.
+    const bool skinny = R >= 9 && (int64_t)(V + 3) / 4 < 2 * (int64_t)dev.num_cus * 8;
+    if (skinny) {
+        switch (R) {
+#define QH_FP8_SKINNY(RR)                                                                     \
+    case RR:                                                                                  \
+        return launch_fp8<RR, 2, 16, 8, 1, W8A8>(W, wscale, x, xscale, H, V, out, dev, stream);
+            QH_FP8_SKINNY(9)
+            QH_FP8_SKINNY(10)
+            QH_FP8_SKINNY(11)
+            QH_FP8_SKINNY(12)
+            QH_FP8_SKINNY(13)
+            QH_FP8_SKINNY(14)
+            QH_FP8_SKINNY(15)
+            QH_FP8_SKINNY(16)
+#undef QH_FP8_SKINNY
+            default:
+                break;
+        }
+    }
     switch (R) {
 #define QH_FP8_CASE(RR, TT, WV, MB, BPC)                                                       \
     case RR:                                                                                  \
