@@ -93,6 +93,32 @@ def test_fp8_8192x1024_all_logits(qh):
         assert np.array_equal(outs[R], outs[16][:R]), R
 
 
+def test_fp8_launch_shape_does_not_change_bits(qh):
+    """9..16-row launches take 2-row bands on heads with fewer than
+    8 * 4 * 2 * CUs vocab rows and 4-row bands above. The same rows computed
+    under both shapes (a head and its leading rows) have identical bits, for
+    W8A16 and W8A8, and lie within the bound."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    v_big = 2 * cus * 8 * 4          # 4-row bands: (V + 3) / 4 is not below the limit
+    v_small = v_big - 4              # 2-row bands
+    H = 1024
+    w, s = _fp8_small(v_big, H, cfg=synth.FP8_32000X4096)
+    wd, sd = dev_u8(w), dev_f32(s)
+    for R in (9, 16):
+        x = synth.activations_bf16(synth.FP8_32000X4096, R, hidden=H, max_rows=R)
+        xd = dev_bf16(x)
+        log(f"[case] fp8 launch shapes V={v_big}/{v_small} R={R}")
+        big = host_bits(qh.fp8_rowscale(wd, sd, xd))
+        small = host_bits(qh.fp8_rowscale(wd[:v_small], sd[:v_small], xd))
+        assert np.array_equal(big[:, :v_small], small), R
+        vidx = sample_vidx(v_big, 600, R)
+        ref, ad = oracle.fp8_rowscale_ref(w[vidx], s[vidx], x)
+        assert_within_bound(big[:, vidx], ref, ad, f"shape check R={R}")
+        big8 = host_bits(qh.w8a8(wd, sd, xd))
+        small8 = host_bits(qh.w8a8(wd[:v_small], sd[:v_small], xd))
+        assert np.array_equal(big8[:, :v_small], small8), R
+
+
 def test_fp8_edge_shapes(qh):
     """Ragged vocab, hidden not a multiple of the 1024-wide segment or the
     4096-wide LDS tile, a single vocab row, and rows spanning chunk borders."""
