@@ -251,7 +251,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the head shards by vocab across GPUs; see the design notes)", file=sys.stderr)
+              "(the head would be split by vocab rows across GPUs, one launch per GPU)", file=sys.stderr)
         sys.exit(2)
 
     import torch
