@@ -96,6 +96,10 @@ fp8_gemv_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
     const int my_r = my_idx / T;
     const int my_t = my_idx - my_r * T;
     const bool writer = ((lane & ((1 << (6 - M)) - 1)) == 0) && (my_idx < N);
+    // Offset (in 16-byte vectors) of activation row 8 in the LDS tile, kept
+    // opaque so the compiler does not fold it back into per-read adds.
+    int hi_rows = 8 * kVecPerTileRow;
+    if constexpr (R > 8) asm volatile("" : "+v"(hi_rows));
 
     for (int sj = 0; sj < nsuper; ++sj) {
         float part[MAXB];
@@ -143,6 +147,10 @@ fp8_gemv_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
                     const int ns = last ? s : ((s + 1 == nseg) ? 0 : s + 1);
                     load_item(nbi, ns, nxt);
                 }
+                // Nothing of the compute below moves above those loads: a
+                // decode of `cur` hoisted above them would need a wait that
+                // also covers the loads just issued.
+                __builtin_amdgcn_sched_barrier(0);
                 if (s == 0) {
 #pragma unroll
                     for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
@@ -156,6 +164,10 @@ fp8_gemv_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
                     e4m3x4_to_bf16(cur[t].w, wb[t][6], wb[t][7]);
                 }
                 const uint4* xrow = xs + s * 128 + lane;
+                // Rows 8 and up lie 64 KiB or more past xrow, beyond the DS
+                // offset field: address them from a second base (one add per
+                // item instead of one per read).
+                const uint4* xrow_hi = xrow + hi_rows;
                 if constexpr (R >= 4) {
                     // Rows in groups of G: for each k pair p, the G * T
                     // accumulators of a group take their dot2 one after the
@@ -170,8 +182,11 @@ fp8_gemv_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
 #pragma unroll
                         for (int g = 0; g < G; ++g) {
                             if (rg + g < R) {
-                                const uint4 xa = xrow[(rg + g) * kVecPerTileRow];
-                                const uint4 xb = xrow[(rg + g) * kVecPerTileRow + 64];
+                                const uint4* xp = (rg + g) < 8
+                                    ? xrow + (rg + g) * kVecPerTileRow
+                                    : xrow_hi + (rg + g - 8) * kVecPerTileRow;
+                                const uint4 xa = xp[0];
+                                const uint4 xb = xp[64];
                                 dst[g][0] = xa.x; dst[g][1] = xa.y; dst[g][2] = xa.z;
                                 dst[g][3] = xa.w; dst[g][4] = xb.x; dst[g][5] = xb.y;
                                 dst[g][6] = xb.z; dst[g][7] = xb.w;

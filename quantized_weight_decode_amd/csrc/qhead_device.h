@@ -117,6 +117,10 @@ __device__ __forceinline__ void permlane32_level(float (&v)[N]) {
             auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]),
                                                       __float_as_uint(v[i + N / 2]), false, false);
             v[i] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+            // The upper half is dead after this level; overwriting it lets
+            // the swap work in place instead of on a copy (worth it from 4
+            // values on; with 2 it only perturbs the scheduling).
+            if constexpr (N >= 4) v[i + N / 2] = __uint_as_float(s[1]);
         }
     } else {
         auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[0]),
@@ -133,6 +137,10 @@ __device__ __forceinline__ void permlane16_level(float (&v)[N]) {
             auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]),
                                                       __float_as_uint(v[i + N / 2]), false, false);
             v[i] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+            // The upper half is dead after this level; overwriting it lets
+            // the swap work in place instead of on a copy (worth it from 4
+            // values on; with 2 it only perturbs the scheduling).
+            if constexpr (N >= 4) v[i + N / 2] = __uint_as_float(s[1]);
         }
     } else {
         auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[0]), __float_as_uint(v[0]),
