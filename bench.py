@@ -124,7 +124,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--rows", type=str, default=None)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="fp8")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the oracle CPU baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -230,9 +230,12 @@ def cpu_baseline(name: str, cfg, rows: list[int], target_s: float):
                 oracle.dequant_nvfp4_bf16(wp, bs, g)
         return time.perf_counter() - t0
 
-    n = 256
-    t = run(n)
-    n = int(min(cfg.vocab, max(n, n * target_s / max(t, 1e-3))))
+    # Size the sample in two steps (about 1 s, then the target): a tiny first
+    # run overstates the time per vocab row (thread start-up, fixed costs).
+    n, t = 256, 0.0
+    for goal in (1.0, target_s):
+        t = run(n)
+        n = int(min(cfg.vocab, max(n, n * goal / max(t, 1e-3))))
     t = run(n)
     bytes_ = sum(algorithmic_bytes(name, n, cfg.hidden, R) for R in rows)
     what = "NVFP4 -> BF16 of those rows" if name == "dequant" else f"rows {rows}"
