@@ -87,6 +87,15 @@ nvfp4_gemv_kernel(const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ bs
     const int my_r = my_idx / T;
     const int my_t = my_idx - my_r * T;
     const bool writer = ((lane & ((1 << (6 - M)) - 1)) == 0) && (my_idx < N);
+    // The DS offset field reaches 64 KiB: activation rows are addressed from
+    // one base per RPB rows, the bases kept opaque so the compiler does not
+    // fold them back into one add per read.
+    constexpr int RPB = 32768 / kF4TileK;
+    int hi_rows = RPB * kF4VecPerTileRow;
+    if constexpr (R > RPB) asm volatile("" : "+v"(hi_rows));
+    auto xrow_at = [&](const uint4* xrow, int r) {
+        return xrow + (r / RPB) * hi_rows + (r % RPB) * kF4VecPerTileRow;
+    };
 
     struct Item {
         uint4 w[T];
@@ -145,7 +154,7 @@ nvfp4_gemv_kernel(const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ bs
                     for (int r = 0; r < R; ++r) {
 #pragma unroll
                         for (int c = 0; c < 4; ++c) {
-                            const uint4 q = xrow[r * kF4VecPerTileRow + 64 * c];
+                            const uint4 q = lds_read16(xrow_at(xrow, r) + 64 * c);
                             xv[r][4 * c + 0] = q.x;
                             xv[r][4 * c + 1] = q.y;
                             xv[r][4 * c + 2] = q.z;
@@ -167,11 +176,12 @@ nvfp4_gemv_kernel(const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ bs
                         const float b1 = __builtin_amdgcn_cvt_f32_fp8(cur.sc[t], 1);
 #pragma unroll
                         for (int r = 0; r < R; ++r) {
-                            float p0 = 0.0f, p1 = 0.0f;
+                            float p0 = dot2_bf16_zero(xv[r][0], wb[0]);
+                            float p1 = dot2_bf16_zero(xv[r][8], wb[8]);
 #pragma unroll
-                            for (int p = 0; p < 8; ++p) p0 = dot2_bf16(xv[r][p], wb[p], p0);
+                            for (int p = 1; p < 8; ++p) p0 = dot2_bf16(xv[r][p], wb[p], p0);
 #pragma unroll
-                            for (int p = 8; p < 16; ++p) p1 = dot2_bf16(xv[r][p], wb[p], p1);
+                            for (int p = 9; p < 16; ++p) p1 = dot2_bf16(xv[r][p], wb[p], p1);
                             float a = acc[r * T + t];
                             a = __builtin_fmaf(b0, p0, a);
                             a = __builtin_fmaf(b1, p1, a);
@@ -198,13 +208,13 @@ nvfp4_gemv_kernel(const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ bs
                 // while row r is computed.
                 uint4 xr[2][4];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) xr[0][c] = xrow[64 * c];
+                for (int c = 0; c < 4; ++c) xr[0][c] = lds_read16(xrow + 64 * c);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     if (r + 1 < R) {
 #pragma unroll
                         for (int c = 0; c < 4; ++c)
-                            xr[(r + 1) & 1][c] = xrow[(r + 1) * kF4VecPerTileRow + 64 * c];
+                            xr[(r + 1) & 1][c] = lds_read16(xrow_at(xrow, r + 1) + 64 * c);
                     }
                     uint32_t xv[16];
 #pragma unroll
@@ -216,11 +226,12 @@ nvfp4_gemv_kernel(const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ bs
                     }
 #pragma unroll
                     for (int t = 0; t < T; ++t) {
-                        float p0 = 0.0f, p1 = 0.0f;
+                        float p0 = dot2_bf16_zero(xv[0], wb[t][0]);
+                        float p1 = dot2_bf16_zero(xv[8], wb[t][8]);
 #pragma unroll
-                        for (int p = 0; p < 8; ++p) p0 = dot2_bf16(xv[p], wb[t][p], p0);
+                        for (int p = 1; p < 8; ++p) p0 = dot2_bf16(xv[p], wb[t][p], p0);
 #pragma unroll
-                        for (int p = 8; p < 16; ++p) p1 = dot2_bf16(xv[p], wb[t][p], p1);
+                        for (int p = 9; p < 16; ++p) p1 = dot2_bf16(xv[p], wb[t][p], p1);
                         float a = acc[r * T + t];
                         a = __builtin_fmaf(bsf[t][0], p0, a);
                         a = __builtin_fmaf(bsf[t][1], p1, a);

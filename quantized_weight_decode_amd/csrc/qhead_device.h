@@ -36,6 +36,15 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(as_bf2(a), as_bf2(b), acc, false);
 }
 
+// a.lo * b.lo + a.hi * b.hi from a zero accumulator: the same instruction
+// with the inline constant 0 as its addend (the compiler's own form copies a
+// zero into the accumulator register first, one more VALU operation).
+__device__ __forceinline__ float dot2_bf16_zero(uint32_t a, uint32_t b) {
+    float r;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // Round a finite FP32 value to BF16, nearest even.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -206,6 +215,15 @@ constexpr int next_pow2(int n) {
 // 16-byte streaming load of weight bytes (read once per launch: non-temporal,
 // so the weight stream does not evict the activations from the caches).
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// A 16-byte LDS read whose words may feed inline asm: the vector passes
+// through an empty asm first, which keeps it one ds_read_b128 (the compiler
+// otherwise splits such a read into 4-byte reads).
+__device__ __forceinline__ uint4 lds_read16(const uint4* p) {
+    u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+    asm("" : "+v"(v));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
     const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
