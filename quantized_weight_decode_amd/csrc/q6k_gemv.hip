@@ -194,7 +194,7 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                     const int mis = (int)(reinterpret_cast<uintptr_t>(p) & 15);
                     const uint8_t* p16 = p - mis;
                     const int ch = min(lane, (mis + nbytes - 1) >> 4);
-                    g[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p16 + 16 * ch));
+                    g[t] = *reinterpret_cast<const u32x4_t*>(p16 + 16 * ch);
                 }
             };
             auto stage = [&](const u32x4_t (&g)[T], int buf) {
