@@ -25,7 +25,9 @@ quantized on the device):
                       the calls rotate over 8 copies of the 132 MB weight
                       (1.06 GB) so that no call finds its weight in the
                       last-level cache, as when a decode step walks the layers
---rows changes the row sweep. Prints one JSON line.
+--rows changes the row sweep. Prints one JSON line; config.read_ceiling is
+the library's plain streaming read (qhead_stream_read) over the same weight
+bytes, and every row count's pct_read_ceiling compares its GB/s with it.
 """
 
 from __future__ import annotations
@@ -120,8 +122,8 @@ def kernel_source_hash(wl: Workload) -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rows", type=str, default=None)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="fp8")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -191,6 +193,53 @@ def algorithmic_bytes(name: str, V: int, H: int, R: int) -> int:
     raise ValueError(name)
 
 
+def measure_read_ceiling(name: str, head, qh, torch, stream, warmup: int = 3,
+                         timed: int = 10) -> dict:
+    """The streaming-read yardstick on the workload's own weight bytes: the
+    library's plain read kernel (qhead_stream_read) over the main weight
+    buffer, median of `timed` calls (rotating over the weight copies where
+    the workload rotates them, so that no read is served from cache)."""
+    if name == "w8a8_silu":
+        bufs = [w for w, _ in head["copies"]]
+    else:
+        bufs = [head[{"fp8": "codes", "w8a8": "codes", "q6k": "blocks"}.get(name, "wp")]]
+    nbytes = bufs[0].numel() * bufs[0].element_size()
+    out = torch.zeros((qh.STREAM_READ_WORDS,), dtype=torch.int32, device=bufs[0].device)
+    # every call rewrites the words of the workgroups it launches: the raw
+    # entry point is timed, without the binding's clear of the output
+    fn, sptr = qh.lib().qhead_stream_read, stream.cuda_stream
+
+    def read(i):
+        st = fn(bufs[i % len(bufs)].data_ptr(), nbytes, out.data_ptr(), sptr)
+        if st != 0:
+            raise RuntimeError(f"qhead_stream_read: {qh.status_string(st)}")
+
+    for i in range(warmup):
+        read(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(timed)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        read(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
+    return {"GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "us_median": round(us, 2),
+            "bytes": nbytes, "kernel": "stream_read_kernel (qhead_stream_read)"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(name: str, cfg, rows: list[int], target_s: float):
     """The oracle timed on a bounded sample of the same workload (vocab rows
     [0, n) of the same head, the same row sweep); returns GB/s of that sample
@@ -243,6 +292,7 @@ def cpu_baseline(name: str, cfg, rows: list[int], target_s: float):
         "value": round(bytes_ / t / 1e9, 4),
         "unit": "GB/s",
         "cores": oracle.num_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"vocab rows [0, {n}) of the same head, {what}, {t:.1f} s "
                   f"(binary64 oracle, OpenMP)",
@@ -354,6 +404,7 @@ def main():
         per_rows["head" if name == "dequant" else str(R)] = {
             "us_median": round(float(np.median(d)) * 1e3, 2),
             "us_min": round(float(d.min()) * 1e3, 2),
+            "us_p90": round(float(np.percentile(d, 90)) * 1e3, 2),
             "GBps": round(gbs, 1),
             "pct_peak": round(gbs / HBM_PEAK_GBS * 100, 1),
             "rows_per_s": round(R / (np.median(d) * 1e-3), 1)}
@@ -361,6 +412,10 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     mean_launch_bytes = step_bytes / len(rows)
     achieved = mean_launch_bytes / (launch_ms.mean() * 1e-3) / 1e9
+
+    read_ceiling = measure_read_ceiling(name, head, qh, torch, stream)
+    for v in per_rows.values():
+        v["pct_read_ceiling"] = round(v["GBps"] / read_ceiling["GBps"] * 100, 1)
 
     traffic = None
     counters = os.path.join(PROFILES, wl.counters)
@@ -375,7 +430,8 @@ def main():
               "vocab": V, "hidden": H, "rows_per_step": rows if name != "dequant" else [],
               "launches_per_step": len(rows), "weight_bytes": algorithmic_bytes(name, V, H, 0),
               "pct_of_hbm_peak": round(value / HBM_PEAK_GBS * 100, 2),
-              "per_rows": per_rows, "wall_s_timed": round(wall, 3),
+              "per_rows": per_rows, "read_ceiling": read_ceiling,
+              "wall_s_timed": round(wall, 3),
               "head_prep_s": round(t_prep, 1)}
     if name != "dequant":
         config["rows_per_s"] = round(sum(rows) / (ms_per_step * 1e-3), 1)

@@ -281,6 +281,19 @@ int qhead_dequant_nvfp4_bf16(const uint8_t* w_packed, const uint8_t* block_scale
 int qhead_dequant_fp4_e8m0_bf16(const uint8_t* w_packed, const uint8_t* scale_e8m0, int64_t total,
                                 int64_t num_groups, uint16_t* out_bf16, void* stream);
 
+/* Measurement support, not part of the GEMV path: reads `bytes` bytes at `p`
+ * once, with coalesced 16-byte non-temporal loads spread over the whole GPU
+ * in the GEMV's per-wave pattern. The time of this call is the
+ * streaming-read ceiling that the GEMV launches are compared with. Each
+ * workgroup stores the XOR of the 32-bit words it read into its own word of
+ * xor_out (device memory, QHEAD_STREAM_READ_WORDS words, cleared by the
+ * caller first); the XOR of all those words is the XOR of the buffer, which
+ * shows every word was read exactly once. p 16-byte aligned; bytes >= 0 and a
+ * multiple of 16 (QHEAD_ERR_SHAPE otherwise); bytes == 0 returns QHEAD_OK and
+ * enqueues nothing. */
+#define QHEAD_STREAM_READ_WORDS 4096
+int qhead_stream_read(const void* p, int64_t bytes, uint32_t* xor_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -70,6 +70,7 @@ _SIGS = {
     "qhead_dequant_nvfp4_bf16": (ctypes.c_int, [_vp, _vp, _i32, _i32, _f32, _vp, _vp]),
     "qhead_dequant_fp4_e8m0_bf16": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, ctypes.c_int64, _vp,
                                                    _vp]),
+    "qhead_stream_read": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp]),
 }
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -122,6 +123,8 @@ def _dev(t: torch.Tensor, name: str, dtypes) -> int:
 
 
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+# words of qhead_stream_read's output (QHEAD_STREAM_READ_WORDS in qhead.h)
+STREAM_READ_WORDS = 4096
 _U8 = (torch.uint8,)
 _F32 = (torch.float32,)
 
@@ -378,3 +381,21 @@ def dequant_fp4_e8m0_bf16(w_packed, scale_e8m0, out=None, stream=None) -> torch.
                                           _stream(stream))
     _check(st, "qhead_dequant_fp4_e8m0_bf16")
     return out
+
+
+def stream_read(buf: torch.Tensor, xor_out=None, stream=None) -> torch.Tensor:
+    """Read the whole of `buf` once (the streaming-read yardstick of the GEMV
+    launches). Returns the int32 device tensor of per-workgroup XORs
+    (STREAM_READ_WORDS words, cleared here first); the XOR of its words is the
+    XOR of all 32-bit words of the buffer."""
+    if xor_out is None:
+        xor_out = torch.zeros((STREAM_READ_WORDS,), dtype=torch.int32, device=buf.device)
+    else:
+        if xor_out.numel() < STREAM_READ_WORDS:
+            raise ValueError(f"xor_out needs {STREAM_READ_WORDS} words")
+        xor_out.zero_()
+    nbytes = buf.numel() * buf.element_size()
+    st = _lib.qhead_stream_read(_dev(buf, "buf", (buf.dtype,)), nbytes,
+                                _dev(xor_out, "xor_out", (torch.int32,)), _stream(stream))
+    _check(st, "qhead_stream_read")
+    return xor_out

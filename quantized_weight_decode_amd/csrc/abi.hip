@@ -438,4 +438,15 @@ int qhead_quantize_fp8_rows(const float* w_f32, int32_t vocab, int32_t hidden, u
                                             static_cast<hipStream_t>(stream)));
 }
 
+int qhead_stream_read(const void* p, int64_t bytes, uint32_t* xor_out, void* stream) {
+    if (bytes < 0 || bytes % 16) return QHEAD_ERR_SHAPE;
+    if (bytes == 0) return QHEAD_OK;
+    if (!p || !xor_out) return QHEAD_ERR_NULL;
+    if (!aligned(p, 16) || !aligned(xor_out, 4)) return QHEAD_ERR_ALIGN;
+    DeviceInfo dev;
+    if (int st = device_or_error(&dev)) return st;
+    return hip_status(run_stream_read(static_cast<const uint8_t*>(p), bytes, xor_out, dev,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

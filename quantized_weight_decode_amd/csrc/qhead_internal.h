@@ -54,6 +54,10 @@ hipError_t run_nvfp4(const uint8_t* Wp, const uint8_t* bs, const uint16_t* x, fl
 hipError_t run_q6k(const uint8_t* blocks, const uint8_t* q8, int R, int H, int V, uint16_t* out,
                    const DeviceInfo& dev, hipStream_t stream);
 
+// Streaming read of a whole buffer (measurement yardstick).
+hipError_t run_stream_read(const uint8_t* p, int64_t bytes, uint32_t* xor_out,
+                           const DeviceInfo& dev, hipStream_t stream);
+
 constexpr int kQ8BlockBytes = 36;
 constexpr int kSiluMaxSlices = 64;
 constexpr int kQ6KBlockBytes = 210;

@@ -31,7 +31,7 @@ MIS = 0x10001
 
 def test_exports_every_declared_function(qh):
     names = qh.header_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(qh.lib(), n), n
     out = subprocess.run(["nm", "-D", "--defined-only", qh.LIB_PATH], capture_output=True,
@@ -198,6 +198,17 @@ def test_dequant_validation(qh):
     assert g(A16 + 4, A16, 96, 3, A16, None) == -3
     assert g(A16, A16, 96, 3, A16 + 8, None) == -3
     assert g(None, None, 0, 3, None, None) == 0
+
+
+def test_stream_read_validation(qh):
+    f = qh.lib().qhead_stream_read
+    assert f(A16, 40, A16, None) == -2                   # not a multiple of 16
+    assert f(A16, -16, A16, None) == -2
+    assert f(None, 64, A16, None) == -1
+    assert f(A16, 64, None, None) == -1
+    assert f(A16 + 8, 64, A16, None) == -3
+    assert f(A16, 64, A16 + 2, None) == -3
+    assert f(None, 0, None, None) == 0
 
 
 def test_header_is_plain_c(qh, tmp_path):
