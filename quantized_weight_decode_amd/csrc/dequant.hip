@@ -75,7 +75,9 @@ dequant_fp4_kernel(const uint32_t* __restrict__ wp, const uint8_t* __restrict__ 
             int64_t i = base + u * kDqThreads + threadIdx.x;
             i = i < groups ? i : groups - 1;  // clamped: the store below is guarded
             w[u] = wp[i];
-            e[u] = sc[i / per_scale];
+            // NVFP4: two groups of 8 per 16-value block scale (a shift, not
+            // a 64-bit division per value)
+            e[u] = sc[kE8M0 ? i / per_scale : i >> 1];
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
