@@ -16,16 +16,20 @@
 
 namespace qh {
 
-__global__ void __launch_bounds__(kQuantThreads)
+// 1024 threads per row: one 8-value vector per thread for hidden sizes up
+// to 8192, so a call of few rows is a single short pass.
+constexpr int kActThreads = 1024;
+
+__global__ void __launch_bounds__(kActThreads)
 quant_act_e4m3_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restrict__ xq,
                       float* __restrict__ sa) {
-    __shared__ uint32_t red[kQuantThreads / 64];
+    __shared__ uint32_t red[kActThreads / 64];
     const int r = blockIdx.x;
     const uint16_t* row = x + (size_t)r * H;
     uint8_t* qrow = xq + (size_t)r * H;
 
     uint32_t m = 0;
-    for (int k = threadIdx.x * 8; k < H; k += kQuantThreads * 8) {
+    for (int k = threadIdx.x * 8; k < H; k += kActThreads * 8) {
         const uint4 v = *reinterpret_cast<const uint4*>(row + k);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -35,18 +39,18 @@ quant_act_e4m3_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restrict
             m = b > m ? b : m;
         }
     }
-    m = block_max_u32(m, red);
+    m = block_max_u32<kActThreads>(m, red);
     const float amax = __uint_as_float(m << 16);
 
     if (amax == 0.0f) {
         if (threadIdx.x == 0) sa[r] = 0.0f;
-        for (int k = threadIdx.x * 8; k < H; k += kQuantThreads * 8)
+        for (int k = threadIdx.x * 8; k < H; k += kActThreads * 8)
             *reinterpret_cast<uint2*>(qrow + k) = make_uint2(0, 0);
         return;
     }
     const float scale = amax / 448.0f;
     if (threadIdx.x == 0) sa[r] = scale;
-    for (int k = threadIdx.x * 8; k < H; k += kQuantThreads * 8) {
+    for (int k = threadIdx.x * 8; k < H; k += kActThreads * 8) {
         const uint4 v = *reinterpret_cast<const uint4*>(row + k);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
         uint32_t packed[2] = {0, 0};
@@ -111,7 +115,7 @@ quant_q8_1_kernel(const uint16_t* __restrict__ x, int rows, int H, uint8_t* __re
 
 hipError_t run_quant_act_e4m3(const uint16_t* x, int rows, int H, uint8_t* xq, float* sa,
                               hipStream_t stream) {
-    hipLaunchKernelGGL(quant_act_e4m3_kernel, dim3(rows), dim3(kQuantThreads), 0, stream, x, H, xq,
+    hipLaunchKernelGGL(quant_act_e4m3_kernel, dim3(rows), dim3(kActThreads), 0, stream, x, H, xq,
                        sa);
     return hipGetLastError();
 }

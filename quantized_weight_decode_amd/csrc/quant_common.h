@@ -9,7 +9,9 @@ constexpr int kQuantThreads = 256;
 
 __device__ __forceinline__ uint32_t bf16_mag(uint32_t two) { return two & 0x7FFFu; }
 
-// Maximum of a per-thread value over the workgroup (kQuantThreads threads).
+// Maximum of a per-thread value over the workgroup (NTHREADS threads; red
+// holds NTHREADS / 64 words).
+template <int NTHREADS = kQuantThreads>
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
     for (int off = 32; off >= 1; off >>= 1) {
         uint32_t o = __shfl_xor(v, off, 64);
@@ -19,7 +21,7 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
     if ((threadIdx.x & 63) == 0) red[wave] = v;
     __syncthreads();
     uint32_t m = red[0];
-    for (int w = 1; w < kQuantThreads / 64; ++w) m = m > red[w] ? m : red[w];
+    for (int w = 1; w < NTHREADS / 64; ++w) m = m > red[w] ? m : red[w];
     return m;
 }
 
