@@ -76,7 +76,8 @@ hipError_t run_stream_read(const uint8_t* p, int64_t bytes, uint32_t* xor_out,
     const int64_t nvec = bytes / 16;
     const int64_t per_block = (int64_t)kReadThreads / kWave * kWave * kReadUnroll;
     int64_t blocks = (nvec + per_block - 1) / per_block;
-    if (blocks > (int64_t)dev.num_cus * kReadBlocksPerCu) blocks = (int64_t)dev.num_cus * kReadBlocksPerCu;
+    const int64_t cap = (int64_t)dev.num_cus * kReadBlocksPerCu;
+    if (blocks > cap) blocks = cap;
     if (blocks > QHEAD_STREAM_READ_WORDS) blocks = QHEAD_STREAM_READ_WORDS;
     hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(kReadThreads), 0, stream, p,
                        nvec, xor_out);
