@@ -299,6 +299,14 @@ static hipError_t launch_fp8(const uint8_t* W, const float* wscale, const void* 
     const int64_t NB = (V + T - 1) / T;
     int64_t blocks = (NB + WAVES - 1) / WAVES;
     if (blocks > (int64_t)dev.num_cus * BPC) blocks = (int64_t)dev.num_cus * BPC;
+    if constexpr (BPC == 1) {
+        // One workgroup per CU: the fewest workgroups that take the same
+        // number of band rounds, so the last round is not a partial one
+        // (4 rows: 204 -> 199 us on the 155136-row head, a few CUs idle);
+        // with several workgroups per CU the full grid is faster.
+        const int64_t rounds = (NB + blocks * WAVES - 1) / (blocks * WAVES);
+        blocks = (NB + rounds * WAVES - 1) / (rounds * WAVES);
+    }
     const int64_t TW = blocks * WAVES;
     const int64_t per_wave = (NB + TW - 1) / TW;
     const int nsuper = (int)((per_wave + MAXB - 1) / MAXB);
