@@ -75,6 +75,8 @@ extern "C" {
                                     for Q6_K, unknown format) */
 #define QHEAD_ERR_DEVICE (-6)    /* current device is not gfx950 */
 #define QHEAD_ERR_HIP (-7)       /* a HIP call or kernel launch failed */
+#define QHEAD_ERR_SCRATCH (-8)   /* the call needs more than the library's fixed
+                                    device scratch (qhead_q6k_static_scratch) */
 
 /* Formats for qhead_plan_chunks / qhead_max_rows_per_launch. */
 #define QHEAD_FMT_FP8 0
@@ -231,6 +233,23 @@ int qhead_q6k_gemv(const uint8_t* blocks, const void* q8, int32_t rows, int32_t 
 int qhead_q6k(const uint8_t* blocks, const void* scales, const uint16_t* x_bf16, int32_t rows,
               int32_t hidden, int32_t vocab, uint16_t* out_bf16, void* workspace,
               size_t workspace_bytes, void* stream);
+
+/* qhead_q6k without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops or harnesses
+ * that forbid hipMalloc). The q8_1 activations of each <= 8-row chunk go to a
+ * fixed device array inside the library, 8 * (QHEAD_Q6K_STATIC_MAX_HIDDEN/32)
+ * blocks of 36 bytes (576 KiB), one copy per GPU, held until the process
+ * ends. The call allocates, frees and clears nothing; its first call on a
+ * device looks up that device's copy of the array. Every call on one GPU
+ * uses the same array, so calls that may overlap on one GPU (different
+ * streams, or host threads) race and must be ordered by the caller. Returns
+ * QHEAD_ERR_SCRATCH, enqueuing nothing, for hidden >
+ * QHEAD_Q6K_STATIC_MAX_HIDDEN; otherwise arguments, results and errors are
+ * those of qhead_q6k, with bit-identical logits. */
+#define QHEAD_Q6K_STATIC_MAX_HIDDEN 65536
+int qhead_q6k_static_scratch(const uint8_t* blocks, const void* scales, const uint16_t* x_bf16,
+                             int32_t rows, int32_t hidden, int32_t vocab, uint16_t* out_bf16,
+                             void* stream);
 
 /* Weight preparation (load time, not the decode path): quantize F32 weights
  * per row to E4M3 with row scales s_v = fl32(amax_v / 448) and codes

@@ -31,7 +31,8 @@ Q6K_BLOCK_BYTES = 210
 
 _STATUS_NAMES = {0: "QHEAD_OK", -1: "QHEAD_ERR_NULL", -2: "QHEAD_ERR_SHAPE",
                  -3: "QHEAD_ERR_ALIGN", -4: "QHEAD_ERR_WORKSPACE", -5: "QHEAD_ERR_ARG",
-                 -6: "QHEAD_ERR_DEVICE", -7: "QHEAD_ERR_HIP"}
+                 -6: "QHEAD_ERR_DEVICE", -7: "QHEAD_ERR_HIP",
+                 -8: "QHEAD_ERR_SCRATCH"}
 
 
 class QheadError(RuntimeError):
@@ -60,6 +61,7 @@ _SIGS = {
     "qhead_q6k_workspace_bytes": (_sz, [_i32]),
     "qhead_q6k_gemv": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "qhead_q6k": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "qhead_q6k_static_scratch": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "qhead_quantize_fp8_rows": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "qhead_silu_mul_bf16": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, _vp, _vp]),
     "qhead_quant_act_silu_e4m3": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
@@ -309,6 +311,25 @@ def q6k(blocks, x, out=None, workspace=None, stream=None) -> torch.Tensor:
                         vocab, _dev(out, "out", _BF16), _dev(workspace, "workspace", _U8),
                         workspace.numel(), _stream(stream))
     _check(st, "qhead_q6k")
+    return out
+
+
+# hidden limit of qhead_q6k_static_scratch (QHEAD_Q6K_STATIC_MAX_HIDDEN in qhead.h)
+Q6K_STATIC_MAX_HIDDEN = 65536
+
+
+def q6k_static_scratch(blocks, x, out=None, stream=None) -> torch.Tensor:
+    """Q6_K logits as q6k(), with the q8_1 activations in the library's fixed
+    per-GPU device array instead of a workspace (nothing is allocated by the
+    call except `out` when it is not given). Calls that may overlap on one GPU
+    race on that array."""
+    vocab = blocks.shape[0]
+    rows, hidden = x.shape
+    out = _out(out, rows, vocab, blocks.device)
+    st = _lib.qhead_q6k_static_scratch(_dev(blocks, "blocks", _U8), None, _dev(x, "x", _BF16),
+                                       rows, hidden, vocab, _dev(out, "out", _BF16),
+                                       _stream(stream))
+    _check(st, "qhead_q6k_static_scratch")
     return out
 
 

@@ -98,6 +98,8 @@ const char* qhead_status_string(int status) {
             return "current device is not gfx950 (MI355X)";
         case QHEAD_ERR_HIP:
             return "HIP call or kernel launch failed";
+        case QHEAD_ERR_SCRATCH:
+            return "size exceeds the library's fixed device scratch";
         default:
             return "unknown status";
     }

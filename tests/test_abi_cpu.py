@@ -31,7 +31,7 @@ MIS = 0x10001
 
 def test_exports_every_declared_function(qh):
     names = qh.header_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(qh.lib(), n), n
     out = subprocess.run(["nm", "-D", "--defined-only", qh.LIB_PATH], capture_output=True,
@@ -41,7 +41,7 @@ def test_exports_every_declared_function(qh):
 
 
 def test_status_strings(qh):
-    for st in range(-7, 1):
+    for st in range(-8, 1):
         assert qh.status_string(st) and qh.status_string(st) != "unknown status"
     assert qh.status_string(-99) == "unknown status"
 
@@ -130,6 +130,23 @@ def test_q6k_validation(qh):
     h = L.qhead_q6k_gemv
     assert h(A16, A16 + 2, 1, 256, 8, A16, None) == -3
     assert h(A16, A16, 0, 256, 8, A16, None) == 0
+
+
+def test_q6k_static_scratch_validation(qh):
+    """The fixed-scratch Q6_K entry point rejects what qhead_q6k rejects, and
+    hidden beyond its scratch (QHEAD_ERR_SCRATCH), before any HIP call."""
+    L = qh.lib()
+    f = L.qhead_q6k_static_scratch
+    big = qh.Q6K_STATIC_MAX_HIDDEN
+    assert f(A16, A16, A16, 1, 512, 8, A16, None) == -5   # scales must be NULL
+    assert f(A16, None, A16, 1, 384, 8, A16, None) == -2  # hidden % 256
+    assert f(A16, None, A16, -1, 512, 8, A16, None) == -2
+    assert f(None, None, A16, 1, 512, 8, A16, None) == -1
+    assert f(A16 + 1, None, A16, 1, 512, 8, A16, None) == -3
+    assert f(A16, None, A16, 1, big + 256, 8, A16, None) == -8
+    assert f(A16, None, A16, 0, big + 256, 8, A16, None) == 0  # rows == 0: nothing to do
+    assert f(A16, None, A16, 0, 512, 8, A16, None) == 0
+    assert "scratch" in qh.status_string(-8)
 
 
 def test_quantize_fp8_rows_validation(qh):
