@@ -37,9 +37,6 @@ int max_rows(int32_t format) {
     }
 }
 
-// Rows per launch of the W8A8 GEMV kernel inside one 128-row chunk.
-constexpr int kW8A8GemvRows = 16;
-
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? QHEAD_OK : QHEAD_ERR_HIP; }
@@ -177,10 +174,11 @@ int qhead_w8a8_gemv(const uint8_t* w_e4m3, const float* row_scale, const uint8_t
     DeviceInfo dev;
     if (int st = device_or_error(&dev)) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const int32_t chunk = max_rows(QHEAD_FMT_W8A8);
     for (int32_t done = 0; done < rows;) {
-        const int32_t m = (rows - done) < kW8A8GemvRows ? (rows - done) : kW8A8GemvRows;
-        hipError_t e = run_fp8_w8a8(w_e4m3, row_scale, xq + (size_t)done * hidden, xscale + done,
-                                    m, hidden, vocab, out_bf16 + (size_t)done * vocab, dev, s);
+        const int32_t m = (rows - done) < chunk ? (rows - done) : chunk;
+        hipError_t e = run_w8a8_gemv(w_e4m3, row_scale, xq + (size_t)done * hidden, xscale + done,
+                                     m, hidden, vocab, out_bf16 + (size_t)done * vocab, dev, s);
         if (e != hipSuccess) return QHEAD_ERR_HIP;
         done += m;
     }
@@ -209,13 +207,9 @@ int qhead_w8a8(const uint8_t* w_e4m3, const float* row_scale, const uint16_t* x_
                                                                   : max_rows(QHEAD_FMT_W8A8);
         hipError_t e = run_quant_act_e4m3(x_bf16 + (size_t)done * hidden, m, hidden, xq, sa, s);
         if (e != hipSuccess) return QHEAD_ERR_HIP;
-        for (int32_t g = 0; g < m;) {
-            const int32_t gm = (m - g) < kW8A8GemvRows ? (m - g) : kW8A8GemvRows;
-            e = run_fp8_w8a8(w_e4m3, row_scale, xq + (size_t)g * hidden, sa + g, gm, hidden, vocab,
-                             out_bf16 + (size_t)(done + g) * vocab, dev, s);
-            if (e != hipSuccess) return QHEAD_ERR_HIP;
-            g += gm;
-        }
+        e = run_w8a8_gemv(w_e4m3, row_scale, xq, sa, m, hidden, vocab,
+                          out_bf16 + (size_t)done * vocab, dev, s);
+        if (e != hipSuccess) return QHEAD_ERR_HIP;
         done += m;
     }
     return QHEAD_OK;
@@ -273,13 +267,9 @@ int qhead_w8a8_silu(const uint8_t* w_e4m3, const float* row_scale, const uint16_
         hipError_t e = run_quant_act_silu_e4m3_split(gate + off, up + off, ld, m, hidden, xq, sa,
                                                      maxbuf, s);
         if (e != hipSuccess) return QHEAD_ERR_HIP;
-        for (int32_t g = 0; g < m;) {
-            const int32_t gm = (m - g) < kW8A8GemvRows ? (m - g) : kW8A8GemvRows;
-            e = run_fp8_w8a8(w_e4m3, row_scale, xq + (size_t)g * hidden, sa + g, gm, hidden, vocab,
-                             out_bf16 + (size_t)(done + g) * vocab, dev, s);
-            if (e != hipSuccess) return QHEAD_ERR_HIP;
-            g += gm;
-        }
+        e = run_w8a8_gemv(w_e4m3, row_scale, xq, sa, m, hidden, vocab,
+                          out_bf16 + (size_t)done * vocab, dev, s);
+        if (e != hipSuccess) return QHEAD_ERR_HIP;
         done += m;
     }
     return QHEAD_OK;

@@ -2,16 +2,12 @@
 //
 // Computes logits[r][v] = bf16(fl32(acc * scale)) with acc = sum_k x[r][k] *
 // e4m3(W[v][k]) in FP32, for the FP8 head with one F32 scale per weight row
-// ("lm_head_fp8_rows.rs": module doc and lm_head_fp8_run, W8A16), and the
-// W8A8 variant that reads the same E4M3 bytes with E4M3 activations and a
-// per-row activation scale ("lm_head_fp8_rows.rs" set_lm_head_w8a8;
-// "w8a8_layer.rs" W8a8Ctx::proj).
+// ("lm_head_fp8_rows.rs": module doc and lm_head_fp8_run, W8A16).
 //
 // Design (MI355X-first; the pages' per-row-count kernels are prior art only):
 //  * One persistent workgroup of WAVES wave64s per CU. The activation rows are
-//    staged once per K-tile into LDS as BF16 (E4M3 activations are decoded to
-//    BF16 exactly while staging), so the weight stream is the only HBM
-//    traffic that scales with vocab.
+//    staged once per K-tile into LDS as BF16, so the weight stream is the
+//    only HBM traffic that scales with vocab.
 //  * Each wave owns bands of T consecutive vocab rows. A band's row is read as
 //    1 KiB segments: lane l loads bytes [16 l, 16 l + 16) of the segment, a
 //    coalesced 16-byte non-temporal load, so every weight byte is fetched
@@ -48,8 +44,8 @@ __device__ __forceinline__ int lds_vec_index(int k_rel) {
     return s * 128 + c * 64 + l;
 }
 
-template <int R, bool W8A8, int NTHREADS>
-__device__ __forceinline__ void stage_tile(uint4* xs, const void* xin, int H, int k0, int nseg) {
+template <int R, int NTHREADS>
+__device__ __forceinline__ void stage_tile(uint4* xs, const uint16_t* xin, int H, int k0, int nseg) {
     const int vec_per_row = nseg * (kSegK / 8);
     const int total = R * vec_per_row;
     for (int idx = threadIdx.x; idx < total; idx += NTHREADS) {
@@ -57,26 +53,16 @@ __device__ __forceinline__ void stage_tile(uint4* xs, const void* xin, int H, in
         const int q = idx - r * vec_per_row;
         const int k = k0 + q * 8;
         uint4 val = make_uint4(0, 0, 0, 0);
-        if (k < H) {
-            if constexpr (W8A8) {
-                const uint2 codes = *reinterpret_cast<const uint2*>(
-                    static_cast<const uint8_t*>(xin) + (size_t)r * H + k);
-                e4m3x4_to_bf16(codes.x, val.x, val.y);
-                e4m3x4_to_bf16(codes.y, val.z, val.w);
-            } else {
-                val = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xin) +
-                                                      (size_t)r * H + k);
-            }
-        }
+        if (k < H) val = *reinterpret_cast<const uint4*>(xin + (size_t)r * H + k);
         xs[r * kVecPerTileRow + lds_vec_index(q * 8)] = val;
     }
 }
 
-template <int R, int T, int WAVES, int MAXB, int BPC, bool W8A8>
+template <int R, int T, int WAVES, int MAXB, int BPC>
 __global__ void __launch_bounds__(WAVES * kWave, (WAVES * BPC + 3) / 4)
 fp8_gemv_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
-                const void* __restrict__ xin, const float* __restrict__ xscale, int H, int V,
-                uint16_t* __restrict__ out, int nsuper) {
+                const uint16_t* __restrict__ xin, int H, int V, uint16_t* __restrict__ out,
+                int nsuper) {
     constexpr int N = T * R;
     constexpr int NP = next_pow2(N);
     constexpr int M = Log2<NP>::value;
@@ -112,7 +98,7 @@ fp8_gemv_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
             const int nseg = (klen + kSegK - 1) / kSegK;
             if (NT > 1 || sj == 0) {
                 __syncthreads();
-                stage_tile<R, W8A8, WAVES * kWave>(xs, xin, H, k0, nseg);
+                stage_tile<R, WAVES * kWave>(xs, xin, H, k0, nseg);
                 __syncthreads();
             }
             // This wave's bands in this super-iteration, walked as one flat
@@ -271,19 +257,12 @@ fp8_gemv_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
             const int v = min(((sj * MAXB + bi) * TW + gw) * T + my_t, V - 1);
             scl[bi] = wscale[v];
         }
-        const float xs_r = W8A8 ? xscale[my_r] : 1.0f;
 #pragma unroll
         for (int bi = 0; bi < MAXB; ++bi) {
             const int band = (sj * MAXB + bi) * TW + gw;
             const int v = band * T + my_t;
-            if (writer && band < NB && v < V) {
-                float y;
-                if constexpr (W8A8)
-                    y = (part[bi] * xs_r) * scl[bi];
-                else
-                    y = part[bi] * scl[bi];
-                out[(size_t)my_r * V + v] = f32_to_bf16_rne(y);
-            }
+            if (writer && band < NB && v < V)
+                out[(size_t)my_r * V + v] = f32_to_bf16_rne(part[bi] * scl[bi]);
         }
     }
 }
@@ -292,10 +271,9 @@ fp8_gemv_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
 
 // A launch shape: T vocab rows per wave, WAVES waves per workgroup, MAXB
 // bands per wave between activation restagings, BPC workgroups per CU.
-template <int R, int T, int WAVES, int MAXB, int BPC, bool W8A8>
-static hipError_t launch_fp8(const uint8_t* W, const float* wscale, const void* x,
-                             const float* xscale, int H, int V, uint16_t* out,
-                             const DeviceInfo& dev, hipStream_t stream) {
+template <int R, int T, int WAVES, int MAXB, int BPC>
+static hipError_t launch_fp8(const uint8_t* W, const float* wscale, const uint16_t* x, int H,
+                             int V, uint16_t* out, const DeviceInfo& dev, hipStream_t stream) {
     const int64_t NB = (V + T - 1) / T;
     int64_t blocks = (NB + WAVES - 1) / WAVES;
     if (blocks > (int64_t)dev.num_cus * BPC) blocks = (int64_t)dev.num_cus * BPC;
@@ -310,8 +288,8 @@ static hipError_t launch_fp8(const uint8_t* W, const float* wscale, const void* 
     const int64_t TW = blocks * WAVES;
     const int64_t per_wave = (NB + TW - 1) / TW;
     const int nsuper = (int)((per_wave + MAXB - 1) / MAXB);
-    hipLaunchKernelGGL((fp8_gemv_kernel<R, T, WAVES, MAXB, BPC, W8A8>), dim3((unsigned)blocks),
-                       dim3(WAVES * kWave), 0, stream, W, wscale, x, xscale, H, V, out, nsuper);
+    hipLaunchKernelGGL((fp8_gemv_kernel<R, T, WAVES, MAXB, BPC>), dim3((unsigned)blocks),
+                       dim3(WAVES * kWave), 0, stream, W, wscale, x, H, V, out, nsuper);
     return hipGetLastError();
 }
 
@@ -320,10 +298,8 @@ static hipError_t launch_fp8(const uint8_t* W, const float* wscale, const void* 
 // loads in flight. From 5 rows on the VALU bounds the kernel: wider bands (T)
 // cut LDS activation reads per weight byte (2R/T bytes) and 8-wave groups
 // leave room for T*R accumulators. The shape never changes a row's bits.
-template <bool W8A8>
-static hipError_t dispatch_fp8(int R, const uint8_t* W, const float* wscale, const void* x,
-                               const float* xscale, int H, int V, uint16_t* out,
-                               const DeviceInfo& dev, hipStream_t stream) {
+hipError_t run_fp8_w8a16(const uint8_t* W, const float* wscale, const uint16_t* x, int R, int H,
+                         int V, uint16_t* out, const DeviceInfo& dev, hipStream_t stream) {
     // Heads with few vocab rows (the SiLU down projection's 7168): with
     // 4-row bands the 9..16-row shape gives a wave fewer than two bands and
     // leaves waves idle; 2-row bands in 16-wave groups keep them busy.
@@ -332,7 +308,7 @@ static hipError_t dispatch_fp8(int R, const uint8_t* W, const float* wscale, con
         switch (R) {
 #define QH_FP8_SKINNY(RR)                                                                     \
     case RR:                                                                                  \
-        return launch_fp8<RR, 2, 16, 8, 1, W8A8>(W, wscale, x, xscale, H, V, out, dev, stream);
+        return launch_fp8<RR, 2, 16, 8, 1>(W, wscale, x, H, V, out, dev, stream);
             QH_FP8_SKINNY(9)
             QH_FP8_SKINNY(10)
             QH_FP8_SKINNY(11)
@@ -349,8 +325,7 @@ static hipError_t dispatch_fp8(int R, const uint8_t* W, const float* wscale, con
     switch (R) {
 #define QH_FP8_CASE(RR, TT, WV, MB, BPC)                                                       \
     case RR:                                                                                  \
-        return launch_fp8<RR, TT, WV, MB, BPC, W8A8>(W, wscale, x, xscale, H, V, out, dev, \
-                                                     stream);
+        return launch_fp8<RR, TT, WV, MB, BPC>(W, wscale, x, H, V, out, dev, stream);
         QH_FP8_CASE(1, 2, 8, 12, 4)
         QH_FP8_CASE(2, 4, 4, 12, 4)
         QH_FP8_CASE(3, 4, 16, 12, 1)
@@ -373,15 +348,5 @@ static hipError_t dispatch_fp8(int R, const uint8_t* W, const float* wscale, con
     }
 }
 
-hipError_t run_fp8_w8a16(const uint8_t* W, const float* s, const uint16_t* x, int R, int H, int V,
-                         uint16_t* out, const DeviceInfo& dev, hipStream_t stream) {
-    return dispatch_fp8<false>(R, W, s, x, nullptr, H, V, out, dev, stream);
-}
-
-hipError_t run_fp8_w8a8(const uint8_t* W, const float* sw, const uint8_t* xq, const float* sa,
-                        int R, int H, int V, uint16_t* out, const DeviceInfo& dev,
-                        hipStream_t stream) {
-    return dispatch_fp8<true>(R, W, sw, xq, sa, H, V, out, dev, stream);
-}
 
 }  // namespace qh

@@ -15,12 +15,13 @@ struct DeviceInfo {
 // Attributes of the current device (cached per device id).
 hipError_t current_device(DeviceInfo* out);
 
-// FP8 family (1 <= R <= 16 rows per launch).
+// FP8 W8A16 (1 <= R <= 16 rows per launch).
 hipError_t run_fp8_w8a16(const uint8_t* W, const float* s, const uint16_t* x, int R, int H, int V,
                          uint16_t* out, const DeviceInfo& dev, hipStream_t stream);
-hipError_t run_fp8_w8a8(const uint8_t* W, const float* sw, const uint8_t* xq, const float* sa,
-                        int R, int H, int V, uint16_t* out, const DeviceInfo& dev,
-                        hipStream_t stream);
+// W8A8 GEMV over quantized activations (1 <= R <= 128 rows per launch).
+hipError_t run_w8a8_gemv(const uint8_t* W, const float* sw, const uint8_t* xq, const float* sa,
+                         int R, int H, int V, uint16_t* out, const DeviceInfo& dev,
+                         hipStream_t stream);
 
 // Activation quantizers and weight preparation.
 hipError_t run_quant_act_e4m3(const uint16_t* x, int rows, int H, uint8_t* xq, float* sa,
