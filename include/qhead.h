@@ -137,7 +137,7 @@ size_t qhead_w8a8_workspace_bytes(int32_t hidden);
  * "w8a8_layer.rs" W8a8Ctx::proj / silu_proj):
  *   out[r][v] = bf16( fl32( fl32(acc * xscale[r]) * row_scale[v] ) ),
  *   acc = sum_k e4m3(xq[r][k]) * e4m3(w[v][k]) in FP32.
- *  xq [rows][hidden] E4M3 codes, 8-byte aligned; xscale [rows] F32; other
+ *  xq [rows][hidden] E4M3 codes, 16-byte aligned; xscale [rows] F32; other
  *  arguments as qhead_fp8_rowscale. */
 int qhead_w8a8_gemv(const uint8_t* w_e4m3, const float* row_scale, const uint8_t* xq,
                     const float* xscale, int32_t rows, int32_t hidden, int32_t vocab,

@@ -168,7 +168,7 @@ int qhead_w8a8_gemv(const uint8_t* w_e4m3, const float* row_scale, const uint8_t
     if (rows < 0 || hidden <= 0 || vocab <= 0 || hidden % 16) return QHEAD_ERR_SHAPE;
     if (rows == 0) return QHEAD_OK;
     if (!w_e4m3 || !row_scale || !xq || !xscale || !out_bf16) return QHEAD_ERR_NULL;
-    if (!aligned(w_e4m3, 16) || !aligned(xq, 8) || !aligned(row_scale, 4) ||
+    if (!aligned(w_e4m3, 16) || !aligned(xq, 16) || !aligned(row_scale, 4) ||
         !aligned(xscale, 4) || !aligned(out_bf16, 2))
         return QHEAD_ERR_ALIGN;
     DeviceInfo dev;

@@ -17,25 +17,31 @@
 // kernel therefore feeds each instruction a weight operand with a single
 // nonzero pair per lane group (a quarter of the instruction's products are
 // useful) and adds the same pairs in the same order as the VALU kernel:
-//   per 4096-k tile, 4 chains per logit; chain c takes the 16-k granules at
-//   tile-local k = 16c + 64i (i = 0, 1, ...), each granule's 8 pairs in k
+//   per 4096-k tile, 8 chains per logit; chain c takes the 16-k granules at
+//   tile-local k = 16c + 128i (i = 0, 1, ...), each granule's 8 pairs in k
 //   order, one dot2-rounded step per pair, starting from +0;
-//   tile sum = (chain0 + chain1) + (chain2 + chain3);
+//   tile sum = ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7));
 //   acc = the tile sums added in tile order;
 //   out = bf16( fl32( fl32(acc * xscale[r]) * wscale[v] ) ).
 // Pairs at k >= hidden have zero activations and leave a chain unchanged.
+// Eight chains keep the VALU kernel's weight reads in 128-byte runs per row
+// (8 lanes x 16 bytes), which stream near the rate of longer runs, while the
+// MFMA kernel holds 8 chains x 8 row tiles of accumulators at 128 rows.
+#include <type_traits>
+#include <utility>
+
 #include "qhead_device.h"
 #include "qhead_internal.h"
 
 namespace qh {
 namespace {
 
-constexpr int kChains = 4;
+constexpr int kChains = 8;
 constexpr int kGranK = 16;                       // k per granule: one 16-byte weight load
-constexpr int kStepK = kChains * kGranK;         // 64: one granule of each chain
-constexpr int kSlabK = 2 * kStepK;               // 128: two granules of each chain
+constexpr int kStepK = kChains * kGranK;         // 128: one granule of each chain
+constexpr int kSlabK = 2 * kStepK;               // 256: two granules of each chain
 constexpr int kW8TileK = 4096;                   // k per reduction tile
-constexpr int kSlabsPerTile = kW8TileK / kSlabK;  // 32
+constexpr int kSlabsPerTile = kW8TileK / kSlabK;  // 16
 constexpr int kTileVec = kW8TileK / 8;           // uint4 of BF16 per row per tile
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -63,9 +69,27 @@ __device__ __forceinline__ void xpose4(uint32_t& r0, uint32_t& r1, uint32_t& r2,
     r3 = e[1];
 }
 
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), unrolled.
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
+// 16 E4M3 bytes -> 8 BF16 pairs (pair p = bytes 2p, 2p+1), exact.
+__device__ __forceinline__ void e4m3x16_to_bf16(const uint4& w, uint32_t (&p)[8]) {
+    e4m3x4_to_bf16(w.x, p[0], p[1]);
+    e4m3x4_to_bf16(w.y, p[2], p[3]);
+    e4m3x4_to_bf16(w.z, p[4], p[5]);
+    e4m3x4_to_bf16(w.w, p[6], p[7]);
+}
+
 // ------------------------------------------------------------ VALU kernel
 
-// Stage tile rows [k0, k0 + 8 * nvec) of R rows of E4M3 codes into LDS as
+// Stage tile columns [k0, k0 + 8 * nvec) of R rows of E4M3 codes into LDS as
 // BF16 (exact), row r at xs + r * kTileVec; k >= H is staged as zero.
 template <int R, int NTHREADS>
 __device__ __forceinline__ void stage_codes_bf16(uint4* xs, const uint8_t* xq, int H, int k0,
@@ -85,10 +109,12 @@ __device__ __forceinline__ void stage_codes_bf16(uint4* xs, const uint8_t* xq, i
     }
 }
 
-// Lanes: c = lane & 3 is the chain, o = lane >> 2 one of 16 vocab slots; a
-// band is 16 slots x T consecutive vocab rows. An item is (band, 64-k step):
-// lane (c, o) loads the 16 weight bytes of granule c of the step for each of
-// its T rows, one coalesced 64-byte piece per row across the four chains.
+// Lanes: chain c = lane bits {0, 1, 3}, vocab slot o = lane bits {2, 4, 5};
+// a band is 8 slots x T consecutive vocab rows. An item is (band, 128-k
+// step): lane (c, o) loads the 16 weight bytes of granule c of the step for
+// each of its T rows, a 128-byte run per row across the eight chains. The
+// chains of a logit sit on lanes l, l^1, l^2, ..., l^11, so the tree is three
+// DPP steps: quad l^1, quad l^2, row_ror:8 (l^8).
 template <int R, int T, int WAVES, int MAXB, int BPC>
 __global__ void __launch_bounds__(WAVES * kWave, (WAVES * BPC + 3) / 4)
 w8a8_valu_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
@@ -96,15 +122,17 @@ w8a8_valu_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
                  uint16_t* __restrict__ out, int nsuper) {
     constexpr int N = T * R;
     constexpr int NP = next_pow2(N);
-    constexpr int NQ = NP >= 4 ? NP / 4 : 1;  // values a lane holds per band after the tree
-    constexpr int BAND = 16 * T;
+    constexpr int NP1 = half_or_one(NP);
+    constexpr int NP2 = half_or_one(NP1);
+    constexpr int NQ = half_or_one(NP2);  // values a lane holds per band after the tree
+    constexpr int BAND = 8 * T;
     static_assert(NP <= 64, "T*R must be <= 64");
     __shared__ uint4 xs[R * kTileVec];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c = lane & 3;
-    const int o = lane >> 2;
+    const int c = (lane & 3) | ((lane >> 1) & 4);
+    const int o = ((lane >> 2) & 1) | ((lane >> 3) & 6);
     const int TW = gridDim.x * WAVES;
     const int gw = blockIdx.x * WAVES + wave;
     const int NB = (V + BAND - 1) / BAND;
@@ -113,6 +141,27 @@ w8a8_valu_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
     // opaque so that rows 8 and up are read from a second base.
     int hi_rows = 8 * kTileVec;
     if constexpr (R > 8) asm volatile("" : "+v"(hi_rows));
+
+    // Index (r * T + t) of the first value this lane holds after the tree:
+    // each of the three levels halves the values a lane holds while more
+    // than one is left (lanes with the level's bit set keep the upper half);
+    // a level reached with one value left sums, and only lanes with that
+    // level's bit clear store.
+    int idx0 = 0;
+    bool writer = true;
+    {
+        int n = NP;
+        const int bits[3] = {lane & 1, (lane >> 1) & 1, (lane >> 3) & 1};
+#pragma unroll
+        for (int lv = 0; lv < 3; ++lv) {
+            if (n >= 2) {
+                n /= 2;
+                idx0 += bits[lv] * n;
+            } else if (bits[lv]) {
+                writer = false;
+            }
+        }
+    }
 
     for (int sj = 0; sj < nsuper; ++sj) {
         float part[MAXB][NQ];
@@ -161,12 +210,7 @@ w8a8_valu_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
                 }
                 uint32_t wb[T][8];
 #pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    e4m3x4_to_bf16(cur[t].x, wb[t][0], wb[t][1]);
-                    e4m3x4_to_bf16(cur[t].y, wb[t][2], wb[t][3]);
-                    e4m3x4_to_bf16(cur[t].z, wb[t][4], wb[t][5]);
-                    e4m3x4_to_bf16(cur[t].w, wb[t][6], wb[t][7]);
-                }
+                for (int t = 0; t < T; ++t) e4m3x16_to_bf16(cur[t], wb[t]);
                 const uint4* xrow = xs + s * (kStepK / 8) + 2 * c;
                 const uint4* xrow_hi = xrow + hi_rows;
                 if constexpr (R >= 4) {
@@ -236,10 +280,9 @@ w8a8_valu_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
                     }
                 }
                 if (s + 1 == nstep) {
-                    // (chain0 + chain1) + (chain2 + chain3): the four chains of a
-                    // logit are the four lanes of a quad.
                     dpp_level<kDppQuadXor1, 1, NP>(acc, lane);
-                    dpp_level<kDppQuadXor2, 2, half_or_one(NP)>(prefix<half_or_one(NP)>(acc), lane);
+                    dpp_level<kDppQuadXor2, 2, NP1>(prefix<NP1>(acc), lane);
+                    dpp_level<kDppRowRor8, 8, NP2>(prefix<NP2>(acc), lane);
 #pragma unroll
                     for (int j = 0; j < MAXB; ++j)
                         if (j == bi) {
@@ -264,19 +307,6 @@ w8a8_valu_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
             if (it < nitems) step(it, bufA, bufB);
         }
 
-        // Index (r * T + t) of the values this lane holds after the tree.
-        int idx0;
-        bool writer;
-        if constexpr (NP >= 4) {
-            idx0 = (c & 1) * (NP / 2) + ((c >> 1) & 1) * (NP / 4);
-            writer = true;
-        } else if constexpr (NP == 2) {
-            idx0 = c & 1;
-            writer = (c >> 1) == 0;
-        } else {
-            idx0 = 0;
-            writer = c == 0;
-        }
 #pragma unroll
         for (int bi = 0; bi < MAXB; ++bi) {
             const int band = (sj * MAXB + bi) * TW + gw;
@@ -298,7 +328,7 @@ w8a8_valu_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
 template <int R, int T, int WAVES, int MAXB, int BPC>
 hipError_t launch_valu(const uint8_t* W, const float* ws, const uint8_t* xq, const float* xs,
                        int H, int V, uint16_t* out, const DeviceInfo& dev, hipStream_t stream) {
-    const int64_t NB = (V + 16 * T - 1) / (16 * T);
+    const int64_t NB = (V + 8 * T - 1) / (8 * T);
     int64_t blocks = (NB + WAVES - 1) / WAVES;
     if (blocks > (int64_t)dev.num_cus * BPC) blocks = (int64_t)dev.num_cus * BPC;
     const int64_t TW = blocks * WAVES;
@@ -311,191 +341,309 @@ hipError_t launch_valu(const uint8_t* W, const float* ws, const uint8_t* xq, con
 
 // ------------------------------------------------------------ MFMA kernel
 
-// Each wave owns tiles of 16 vocab rows (the B columns of the MFMA) for all
-// 16 * RT activation rows (RT row tiles, the A rows; rows >= R are zero).
-// The workgroup walks the hidden dimension in 128-k slabs: per slab each
-// chain has two granules (A at k_s + 16c, B at k_s + 64 + 16c). The
-// activations of a slab are staged in LDS by the whole workgroup as the
-// dense A operands, [chain][lane group g][row] x 16 bytes holding the BF16
-// pairs (A pair g, A pair 4+g, B pair g, B pair 4+g) -- the pairs that step
-// g of instructions 0..3 multiply. The weights are loaded per lane (lane
-// group g: 16 bytes of chain g, granule A, then granule B), converted to
-// BF16 pairs and transposed across lane groups so that dword q of lane group
-// g holds the same pair of the weight row; instruction t then uses a weight
-// operand holding only dword t, so its step g adds exactly that one pair.
-template <int RT, int WAVES, int BPC>
-__global__ void __launch_bounds__(WAVES * kWave, (WAVES * BPC + 3) / 4)
+// A workgroup holds VTW vocab tiles of 16 rows (the B columns of the MFMA)
+// and computes them for all 16 * RT activation rows (RT row tiles, the A
+// rows; rows >= R are zero). CS waves share a vocab tile: wave h owns chains
+// h * 8/CS .. (h + 1) * 8/CS - 1 of it. The workgroup walks the hidden
+// dimension in 256-k slabs: per slab each chain c has two granules, A at
+// k_s + 16c and B at k_s + 128 + 16c. The activations of a slab are staged
+// in LDS by the whole workgroup as the dense A operands, [chain][lane group
+// g][row] x 16 bytes holding the BF16 pairs (A pair g, A pair 4+g, B pair g,
+// B pair 4+g) -- the pairs that step g of instructions 0..3 multiply. The
+// weights of four chains come from two 16-byte loads per lane (lane group
+// g: chain g of the group, granule A, then B), or, with two chains per
+// wave, those of a chain pair from one load (lane group g: chain g/2,
+// granule g & 1); they are converted to BF16 pairs and transposed across
+// lane groups so that dword q of lane group g holds the pair that
+// instruction q's step g multiplies; instruction t then uses a weight
+// operand holding only dword t, so its step g adds exactly that one pair. At the end of each 4096-k tile the chains go
+// through the tree (across the waves of a tile through LDS) and restart
+// from zero.
+template <int RT, int VTW, int CS, int PF>
+__global__ void __launch_bounds__(VTW * CS * kWave, (VTW * CS + 3) / 4)
 w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
                  const uint8_t* __restrict__ xq, const float* __restrict__ xscale, int R, int H,
                  int V, uint16_t* __restrict__ out, int nrounds) {
+    constexpr int WAVES = VTW * CS;
     constexpr int RP = 16 * RT;
     constexpr int NTHREADS = WAVES * kWave;
-    constexpr int SLAB_VEC = kChains * 4 * RP;  // uint4 per staged slab
+    constexpr int NCW = kChains / CS;            // chains per wave
+    constexpr int LG = NCW >= 4 ? 4 : 2;         // chains per weight-load group
+    constexpr int NLW = 2 * NCW / LG;            // 16-byte weight loads per slab
+    constexpr int SLAB_VEC = kChains * 4 * RP;   // uint4 per staged slab
     constexpr int UNITS = kChains * RP;          // (chain, row) staging units per slab
     constexpr int UPT = (UNITS + NTHREADS - 1) / NTHREADS;
+    static_assert(CS == 1 || CS == 2 || CS == 4, "8 chains over 1, 2 or 4 waves");
+    // the tree's exchange reuses a slab buffer: (CS - 1) partial sums per tile
+    static_assert((CS - 1) * VTW * RT * kWave <= SLAB_VEC, "exchange fits a slab buffer");
     __shared__ uint4 xs[2][SLAB_VEC];
+    __shared__ float xsc[RP];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int vt = wave / CS;
+    const int h = wave - vt * CS;
     const int i16 = lane & 15;
     const int g = lane >> 4;
     const int ntiles = (V + 15) / 16;
     const int NS = (H + kSlabK - 1) / kSlabK;
     const int total = nrounds * NS;
 
-    // Staging of slab `it % NS`: unit u = (chain, row) with rows fastest, so
-    // consecutive threads write consecutive 16-byte LDS words.
-    auto stage_load = [&](int it, uint4(&st)[UPT][2]) {
-        const int k_s = (it % NS) * kSlabK;
+    // Staging of slab `s`: unit u = (chain, row), rows fastest, so
+    // consecutive threads write consecutive 16-byte LDS words. The loads use
+    // clamped addresses and are consumed only when the slab is written
+    // (rows >= R and k >= H become zero there), so they stay in flight.
+    auto stage_load = [&](int s, uint4(&st)[UPT][2]) __attribute__((always_inline)) {
+        const int k_s = s * kSlabK;
 #pragma unroll
         for (int j = 0; j < UPT; ++j) {
-            const int u = threadIdx.x + j * NTHREADS;
-            const int r = u % RP;
+            const int u = min((int)threadIdx.x + j * NTHREADS, UNITS - 1);
+            const int r = min(u % RP, R - 1);
             const int X = u / RP;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int k = k_s + h * kStepK + X * kGranK;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (u < UNITS && r < R && k < H) {
-                    const uint2* p = reinterpret_cast<const uint2*>(xq + (size_t)r * H + k);
-                    const uint2 lo = p[0], hi = p[1];
-                    v = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                }
-                st[j][h] = v;
+            for (int gb = 0; gb < 2; ++gb) {
+                const int k = min(k_s + gb * kStepK + X * kGranK, H - 16);
+                st[j][gb] = *reinterpret_cast<const uint4*>(xq + (size_t)r * H + k);
             }
         }
     };
-    auto stage_write = [&](const uint4(&st)[UPT][2], uint4* dst) {
+    auto stage_write = [&](int s, const uint4(&st)[UPT][2], uint4* dst) __attribute__((always_inline)) {
+        const int k_s = s * kSlabK;
 #pragma unroll
         for (int j = 0; j < UPT; ++j) {
-            const int u = threadIdx.x + j * NTHREADS;
-            if (u < UNITS) {
+            const int u = (int)threadIdx.x + j * NTHREADS;
+            if (UNITS % NTHREADS == 0 || u < UNITS) {
                 const int r = u % RP;
                 const int X = u / RP;
                 uint32_t pa[8], pb[8];
-                e4m3x4_to_bf16(st[j][0].x, pa[0], pa[1]);
-                e4m3x4_to_bf16(st[j][0].y, pa[2], pa[3]);
-                e4m3x4_to_bf16(st[j][0].z, pa[4], pa[5]);
-                e4m3x4_to_bf16(st[j][0].w, pa[6], pa[7]);
-                e4m3x4_to_bf16(st[j][1].x, pb[0], pb[1]);
-                e4m3x4_to_bf16(st[j][1].y, pb[2], pb[3]);
-                e4m3x4_to_bf16(st[j][1].z, pb[4], pb[5]);
-                e4m3x4_to_bf16(st[j][1].w, pb[6], pb[7]);
+                e4m3x16_to_bf16(st[j][0], pa);
+                e4m3x16_to_bf16(st[j][1], pb);
+                const bool oka = r < R && k_s + X * kGranK < H;
+                const bool okb = r < R && k_s + kStepK + X * kGranK < H;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    pa[i] = oka ? pa[i] : 0u;
+                    pb[i] = okb ? pb[i] : 0u;
+                }
 #pragma unroll
                 for (int gg = 0; gg < 4; ++gg)
                     dst[(X * 4 + gg) * RP + r] = make_uint4(pa[gg], pa[4 + gg], pb[gg], pb[4 + gg]);
             }
         }
     };
-    auto tile_of = [&](int it) { return ((it / NS) * (int)gridDim.x + (int)blockIdx.x) * WAVES + wave; };
-    auto wload = [&](int it, uint4(&dst)[2]) {
+    const int nblk = gridDim.x;
+    auto tile_of = [&](int it) { return ((it / NS) * nblk + (int)blockIdx.x) * VTW + vt; };
+    // Weight loads of slab `it`. LG = 4: two loads per group of four chains
+    // (lane group g: chain g of the group; granule A, then B), a 64-byte run
+    // per row. LG = 2: one load per chain pair (lane group g: chain g/2 of
+    // the pair, granule g & 1), two 32-byte runs per row.
+    auto wload = [&](int it, uint4(&dst)[NLW]) __attribute__((always_inline)) {
         const int k_s = (it % NS) * kSlabK;
         const int v = min(tile_of(it) * 16 + i16, V - 1);
         const uint8_t* wrow = W + (size_t)v * H;
-        dst[0] = load_stream16(wrow + min(k_s + g * kGranK, H - 16));
-        dst[1] = load_stream16(wrow + min(k_s + kStepK + g * kGranK, H - 16));
+#pragma unroll
+        for (int j = 0; j < NLW; ++j) {
+            int X, gb;
+            if constexpr (LG == 4) {
+                X = h * NCW + (j >> 1) * 4 + g;
+                gb = j & 1;
+            } else {
+                X = h * NCW + 2 * j + (g >> 1);
+                gb = g & 1;
+            }
+            dst[j] = load_stream16(wrow + min(k_s + gb * kStepK + X * kGranK, H - 16));
+        }
     };
 
-    f32x4_t acc[kChains][RT];
+    f32x4_t acc[NCW][RT];
     f32x4_t part[RT];
-    uint4 st[UPT][2];
-    uint4 wcur[2], wnxt[2];
-    if (total > 0) {
-        stage_load(0, st);
-        stage_write(st, xs[0]);
-        wload(0, wcur);
-    }
+    // Activation codes of the next two slabs (slot n % 2 holds slab n's).
+    uint4 st[2][UPT][2];
+    // Weights of PF slabs in flight: slot (it % PF) holds slab it's bytes.
+    uint4 wb[PF][NLW];
+#pragma unroll
+    for (int X = 0; X < NCW; ++X)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[X][rt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) part[rt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int r = threadIdx.x; r < RP; r += NTHREADS) xsc[r] = r < R ? xscale[r] : 0.0f;
+    stage_load(0, st[0]);
+    stage_write(0, st[0], xs[0]);
+    stage_load(min(1, total - 1) % NS, st[1]);
+#pragma unroll
+    for (int p = 0; p + 1 < PF; ++p) wload(min(p, total - 1), wb[p]);
     __syncthreads();
-#pragma unroll 1
-    for (int it = 0; it < total; ++it) {
+
+    // One slab: SL = it % PF (a compile-time slot, the loop is unrolled by PF).
+    auto slab = [&](auto sl_tag, int it) __attribute__((always_inline)) {
+        constexpr int SL = decltype(sl_tag)::value;
+        static_assert(PF % 2 == 0, "the staging slots follow it % 2");
         const int s = it % NS;
         const bool more = it + 1 < total;
-        if (more) {
-            stage_load(it + 1, st);
-            wload(it + 1, wnxt);
-        }
-        if (s % kSlabsPerTile == 0) {
+        // Activation codes two slabs ahead (their slot held slab it's codes,
+        // already in LDS), then the weights PF - 1 slabs ahead.
+        // Unconditional (clamped to the last slab): a load inside a branch
+        // would make the compiler wait for every load in flight.
+        stage_load(min(it + 2, total - 1) % NS, st[SL % 2]);
+        wload(min(it + PF - 1, total - 1), wb[(SL + PF - 1) % PF]);
+        // This tile's row scale, loaded every slab so that no load sits in
+        // the branch that stores (a load there stalls the prefetches above).
+        const float sw = wscale[min(tile_of(it) * 16 + i16, V - 1)];
+        uint4* xb = xs[it & 1];
+        // Chain XL's weight operand bq[t] holds only dword t; o[] are the
+        // BF16 pairs after the transposes.
+        auto chain_mfma = [&](int XL, const uint4(&bq)[4]) __attribute__((always_inline)) {
+            const int X = h * NCW + XL;
+            uint4 a[RT];
 #pragma unroll
-            for (int X = 0; X < kChains; ++X)
+            for (int rt = 0; rt < RT; ++rt) a[rt] = xb[(X * 4 + g) * RP + rt * 16 + i16];
+            // Instruction t of every row tile before instruction t + 1:
+            // consecutive MFMAs use different accumulators.
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) acc[XL][rt] = mfma_bf16(a[rt], bq[t], acc[XL][rt]);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        if constexpr (LG == 4) {
+#pragma unroll
+            for (int j = 0; j < NCW / 4; ++j) {
+                // Four chains: a1[Q] = pair g of granule A of chain Q's row,
+                // a1[4+Q] its pair 4+g; a2[] the same for granule B.
+                uint32_t a1[8], a2[8];
+                e4m3x16_to_bf16(wb[SL][2 * j], a1);
+                e4m3x16_to_bf16(wb[SL][2 * j + 1], a2);
+                xpose4(a1[0], a1[1], a1[2], a1[3]);
+                xpose4(a1[4], a1[5], a1[6], a1[7]);
+                xpose4(a2[0], a2[1], a2[2], a2[3]);
+                xpose4(a2[4], a2[5], a2[6], a2[7]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint4 bq[4] = {make_uint4(a1[q], 0, 0, 0), make_uint4(0, a1[4 + q], 0, 0),
+                                         make_uint4(0, 0, a2[q], 0), make_uint4(0, 0, 0, a2[4 + q])};
+                    chain_mfma(4 * j + q, bq);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NCW / 2; ++j) {
+                // Chains 2j, 2j+1: o[Q] holds pair g of granule Q's row
+                // (Q = 2c + granule), o[4 + Q] its pair 4 + g.
+                uint32_t o[8];
+                e4m3x16_to_bf16(wb[SL][j], o);
+                xpose4(o[0], o[1], o[2], o[3]);
+                xpose4(o[4], o[5], o[6], o[7]);
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const uint4 bq[4] = {make_uint4(o[2 * c], 0, 0, 0),
+                                         make_uint4(0, o[4 + 2 * c], 0, 0),
+                                         make_uint4(0, 0, o[2 * c + 1], 0),
+                                         make_uint4(0, 0, 0, o[5 + 2 * c])};
+                    chain_mfma(2 * j + c, bq);
+                }
+            }
+        }
+        if (more) stage_write((it + 1) % NS, st[(SL + 1) % 2], xs[(it + 1) & 1]);
+        // End of a 4096-k tile (or of the hidden dimension): the tree
+        // ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7)) -- each wave its
+        // chains' subtree, the workgroup's waves of a tile through LDS in
+        // this slab's (consumed) buffer -- then the tile sum in tile order,
+        // and the chains restart from zero.
+        if ((s + 1) % kSlabsPerTile == 0 || s + 1 == NS) {
+            f32x4_t sub[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                if constexpr (NCW == 8)
+                    sub[rt] = ((acc[0][rt] + acc[1][rt]) + (acc[2][rt] + acc[3][rt])) +
+                              ((acc[4][rt] + acc[5][rt]) + (acc[6][rt] + acc[7][rt]));
+                else if constexpr (NCW == 4)
+                    sub[rt] = (acc[0][rt] + acc[1][rt]) + (acc[2][rt] + acc[3][rt]);
+                else
+                    sub[rt] = acc[0][rt] + acc[1][rt];
+            }
+            if constexpr (CS > 1) {
+                f32x4_t* xch = reinterpret_cast<f32x4_t*>(xb);
+                __syncthreads();  // every wave is done reading this slab's buffer
+                if (h > 0) {
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        xch[(((h - 1) * VTW + vt) * RT + rt) * kWave + lane] = sub[rt];
+                }
+                __syncthreads();
+                if (h == 0) {
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) {
+                        const f32x4_t s1 = xch[((0 * VTW + vt) * RT + rt) * kWave + lane];
+                        if constexpr (CS == 2) {
+                            sub[rt] = sub[rt] + s1;
+                        } else {
+                            const f32x4_t s2 = xch[((1 * VTW + vt) * RT + rt) * kWave + lane];
+                            const f32x4_t s3 = xch[((2 * VTW + vt) * RT + rt) * kWave + lane];
+                            sub[rt] = (sub[rt] + s1) + (s2 + s3);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+            if (h == 0) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    part[rt] = (s < kSlabsPerTile) ? sub[rt] : part[rt] + sub[rt];
+            }
+#pragma unroll
+            for (int X = 0; X < NCW; ++X)
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) acc[X][rt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         }
-        // Weights: BF16 pairs of chain g's granules, then the transposes.
-        uint32_t a1[8], a2[8];
-        e4m3x4_to_bf16(wcur[0].x, a1[0], a1[1]);
-        e4m3x4_to_bf16(wcur[0].y, a1[2], a1[3]);
-        e4m3x4_to_bf16(wcur[0].z, a1[4], a1[5]);
-        e4m3x4_to_bf16(wcur[0].w, a1[6], a1[7]);
-        e4m3x4_to_bf16(wcur[1].x, a2[0], a2[1]);
-        e4m3x4_to_bf16(wcur[1].y, a2[2], a2[3]);
-        e4m3x4_to_bf16(wcur[1].z, a2[4], a2[5]);
-        e4m3x4_to_bf16(wcur[1].w, a2[6], a2[7]);
-        xpose4(a1[0], a1[1], a1[2], a1[3]);
-        xpose4(a1[4], a1[5], a1[6], a1[7]);
-        xpose4(a2[0], a2[1], a2[2], a2[3]);
-        xpose4(a2[4], a2[5], a2[6], a2[7]);
-        const uint4* xb = xs[it & 1];
-#pragma unroll
-        for (int X = 0; X < kChains; ++X) {
-            const uint4 b0 = make_uint4(a1[X], 0, 0, 0);
-            const uint4 b1 = make_uint4(0, a1[4 + X], 0, 0);
-            const uint4 b2 = make_uint4(0, 0, a2[X], 0);
-            const uint4 b3 = make_uint4(0, 0, 0, a2[4 + X]);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const uint4 a = xb[(X * 4 + g) * RP + rt * 16 + i16];
-                f32x4_t d = acc[X][rt];
-                d = mfma_bf16(a, b0, d);
-                d = mfma_bf16(a, b1, d);
-                d = mfma_bf16(a, b2, d);
-                d = mfma_bf16(a, b3, d);
-                acc[X][rt] = d;
-            }
-        }
-        if (more) stage_write(st, xs[(it + 1) & 1]);
-        // End of a 4096-k tile (or of the hidden dimension): the tree, then the
-        // tile sum in tile order.
-        if ((s + 1) % kSlabsPerTile == 0 || s + 1 == NS) {
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const f32x4_t sum = (acc[0][rt] + acc[1][rt]) + (acc[2][rt] + acc[3][rt]);
-                part[rt] = (s < kSlabsPerTile) ? sum : part[rt] + sum;
-            }
-        }
-        if (s + 1 == NS) {
+        if (s + 1 == NS && h == 0) {
             const int tile = tile_of(it);
             const int v = tile * 16 + i16;
             if (tile < ntiles && v < V) {
-                const float sw = wscale[v];
+                // Row offsets computed here, once per vocab tile: an opaque
+                // copy of V keeps them from being hoisted out of the slab
+                // loop, where they would hold registers for the whole loop.
+                int Vq = V;
+                asm volatile("" : "+s"(Vq));
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = rt * 16 + g * 4 + e;
                         if (r < R) {
-                            const float y = (part[rt][e] * xscale[r]) * sw;
-                            out[(size_t)r * V + v] = f32_to_bf16_rne(y);
+                            const float y = (part[rt][e] * xsc[r]) * sw;
+                            out[(size_t)r * Vq + v] = f32_to_bf16_rne(y);
                         }
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
         __syncthreads();
-        wcur[0] = wnxt[0];
-        wcur[1] = wnxt[1];
-    }
+    };
+
+    int it = 0;
+#pragma unroll 1
+    for (; it + PF <= total; it += PF)
+        static_for<PF>([&](auto sl) __attribute__((always_inline)) {
+            slab(sl, it + decltype(sl)::value);
+        });
+    static_for<PF>([&](auto sl) __attribute__((always_inline)) {
+        if (it + decltype(sl)::value < total) slab(sl, it + decltype(sl)::value);
+    });
 }
 
-template <int RT, int WAVES, int BPC>
+template <int RT, int VTW, int CS, int PF>
 hipError_t launch_mfma(const uint8_t* W, const float* ws, const uint8_t* xq, const float* xs,
                        int R, int H, int V, uint16_t* out, const DeviceInfo& dev,
                        hipStream_t stream) {
     const int64_t ntiles = (V + 15) / 16;
-    int64_t blocks = (ntiles + WAVES - 1) / WAVES;
-    if (blocks > (int64_t)dev.num_cus * BPC) blocks = (int64_t)dev.num_cus * BPC;
-    const int nrounds = (int)((ntiles + blocks * WAVES - 1) / (blocks * WAVES));
-    hipLaunchKernelGGL((w8a8_mfma_kernel<RT, WAVES, BPC>), dim3((unsigned)blocks),
-                       dim3(WAVES * kWave), 0, stream, W, ws, xq, xs, R, H, V, out, nrounds);
+    int64_t blocks = (ntiles + VTW - 1) / VTW;
+    if (blocks > (int64_t)dev.num_cus) blocks = (int64_t)dev.num_cus;
+    const int nrounds = (int)((ntiles + blocks * VTW - 1) / (blocks * VTW));
+    hipLaunchKernelGGL((w8a8_mfma_kernel<RT, VTW, CS, PF>), dim3((unsigned)blocks),
+                       dim3(VTW * CS * kWave), 0, stream, W, ws, xq, xs, R, H, V, out, nrounds);
     return hipGetLastError();
 }
 
@@ -529,23 +677,26 @@ hipError_t run_w8a8_gemv(const uint8_t* W, const float* sw, const uint8_t* xq, c
             break;
     }
     if (R < 16 || R > 128) return hipErrorInvalidValue;
+    // Launch shapes <RT, vocab tiles per workgroup, waves per tile, weight
+    // slabs in flight>, eight waves per workgroup (two per SIMD): up to 32
+    // rows one wave per tile, up to 64 two, above four (2 chains each).
     switch ((R + 15) / 16) {
         case 1:
-            return launch_mfma<1, 8, 1>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma<1, 8, 1, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
         case 2:
-            return launch_mfma<2, 8, 1>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma<2, 8, 1, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
         case 3:
-            return launch_mfma<3, 8, 1>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma<3, 4, 2, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
         case 4:
-            return launch_mfma<4, 8, 1>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma<4, 4, 2, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
         case 5:
-            return launch_mfma<5, 4, 1>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma<5, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
         case 6:
-            return launch_mfma<6, 4, 1>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma<6, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
         case 7:
-            return launch_mfma<7, 4, 1>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma<7, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
         default:
-            return launch_mfma<8, 4, 1>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma<8, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
     }
 }
 

@@ -103,6 +103,7 @@ def test_w8a8_validation(qh):
     assert g(A16, 0, 64, A16, A16, None) == 0
     h = L.qhead_w8a8_gemv
     assert h(A16, A16, A16, None, 1, 64, 8, A16, None) == -1
+    assert h(A16, A16, A16 + 8, A16, 1, 64, 8, A16, None) == -3  # xq 16-byte aligned
     assert h(A16, A16, A16, A16, 0, 64, 8, A16, None) == 0
 
 
