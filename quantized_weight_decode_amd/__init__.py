@@ -146,16 +146,39 @@ def plan_chunks(fmt: int, rows: int) -> list[int]:
     return [buf[i] for i in range(n2)]
 
 
+def _shape(t, name: str, shape) -> None:
+    """ValueError unless `t` is a tensor of exactly `shape` (None: any extent).
+    The library reads and writes by the sizes it is given, so a tensor of
+    another shape would be read or written out of bounds."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    got = tuple(t.shape)
+    if len(got) != len(shape) or any(e is not None and a != e for a, e in zip(got, shape)):
+        want = tuple("*" if e is None else e for e in shape)
+        raise ValueError(f"{name} has shape {got}, expected {want}")
+
+
+def _min_numel(t, name: str, n: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.numel() < n:
+        raise ValueError(f"{name} has {t.numel()} elements, needs at least {n}")
+
+
 def _out(out, rows, vocab, device):
     if out is None:
-        out = torch.empty((rows, vocab), dtype=torch.bfloat16, device=device)
+        return torch.empty((rows, vocab), dtype=torch.bfloat16, device=device)
+    _shape(out, "out", (rows, vocab))
     return out
 
 
 def fp8_rowscale(w: torch.Tensor, row_scale: torch.Tensor, x: torch.Tensor, out=None,
                  stream=None) -> torch.Tensor:
     """logits[rows, vocab] (BF16) from FP8 E4M3 weights [vocab, hidden] with F32 row scales."""
+    _shape(w, "w", (None, None))
     vocab, hidden = w.shape
+    _shape(row_scale, "row_scale", (vocab,))
+    _shape(x, "x", (None, hidden))
     rows = x.shape[0]
     out = _out(out, rows, vocab, w.device)
     st = _lib.qhead_fp8_rowscale(_dev(w, "w", _U8), _dev(row_scale, "row_scale", _F32),
@@ -167,11 +190,14 @@ def fp8_rowscale(w: torch.Tensor, row_scale: torch.Tensor, x: torch.Tensor, out=
 
 def quant_act_e4m3(x: torch.Tensor, xq=None, xscale=None, stream=None):
     """Per-row E4M3 activations: returns (xq uint8 [rows, hidden], xscale f32 [rows])."""
+    _shape(x, "x", (None, None))
     rows, hidden = x.shape
     if xq is None:
         xq = torch.empty((rows, hidden), dtype=torch.uint8, device=x.device)
     if xscale is None:
         xscale = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    _shape(xq, "xq", (rows, hidden))
+    _shape(xscale, "xscale", (rows,))
     st = _lib.qhead_quant_act_e4m3(_dev(x, "x", _BF16), rows, hidden, _dev(xq, "xq", _U8),
                                    _dev(xscale, "xscale", _F32), _stream(stream))
     _check(st, "qhead_quant_act_e4m3")
@@ -187,8 +213,12 @@ def w8a8_workspace(hidden: int, device) -> torch.Tensor:
 
 
 def w8a8_gemv(w, row_scale, xq, xscale, out=None, stream=None) -> torch.Tensor:
+    _shape(w, "w", (None, None))
     vocab, hidden = w.shape
+    _shape(row_scale, "row_scale", (vocab,))
+    _shape(xq, "xq", (None, hidden))
     rows = xq.shape[0]
+    _shape(xscale, "xscale", (rows,))
     out = _out(out, rows, vocab, w.device)
     st = _lib.qhead_w8a8_gemv(_dev(w, "w", _U8), _dev(row_scale, "row_scale", _F32),
                               _dev(xq, "xq", _U8), _dev(xscale, "xscale", _F32), rows, hidden,
@@ -199,11 +229,15 @@ def w8a8_gemv(w, row_scale, xq, xscale, out=None, stream=None) -> torch.Tensor:
 
 def w8a8(w, row_scale, x, out=None, workspace=None, stream=None) -> torch.Tensor:
     """W8A8 logits: per-row E4M3 activations, then FP8 x FP8 over the same weight bytes."""
+    _shape(w, "w", (None, None))
     vocab, hidden = w.shape
+    _shape(row_scale, "row_scale", (vocab,))
+    _shape(x, "x", (None, hidden))
     rows = x.shape[0]
     out = _out(out, rows, vocab, w.device)
     if workspace is None:
         workspace = w8a8_workspace(hidden, w.device)
+    _min_numel(workspace, "workspace", w8a8_workspace_bytes(hidden))
     st = _lib.qhead_w8a8(_dev(w, "w", _U8), _dev(row_scale, "row_scale", _F32),
                          _dev(x, "x", _BF16), rows, hidden, vocab, _dev(out, "out", _BF16),
                          _dev(workspace, "workspace", _U8), workspace.numel(), _stream(stream))
@@ -212,10 +246,14 @@ def w8a8(w, row_scale, x, out=None, workspace=None, stream=None) -> torch.Tensor
 
 
 def _silu_shapes(gate, up, hidden):
-    if gate.shape != up.shape or gate.dim() != 2:
+    _shape(gate, "gate", (None, None))
+    if gate.shape != up.shape:
         raise ValueError("gate and up must be [rows, ld] tensors of one shape")
     rows, ld = gate.shape
-    return rows, ld, ld if hidden is None else int(hidden)
+    hidden = ld if hidden is None else int(hidden)
+    if hidden > ld:
+        raise ValueError(f"hidden {hidden} exceeds the row length {ld} of gate and up")
+    return rows, ld, hidden
 
 
 def silu_mul_bf16(gate, up, out=None, stream=None) -> torch.Tensor:
@@ -224,6 +262,7 @@ def silu_mul_bf16(gate, up, out=None, stream=None) -> torch.Tensor:
         raise ValueError("gate and up must have one shape")
     if out is None:
         out = torch.empty(gate.shape, dtype=torch.bfloat16, device=gate.device)
+    _shape(out, "out", tuple(gate.shape))
     st = _lib.qhead_silu_mul_bf16(_dev(gate, "gate", _BF16), _dev(up, "up", _BF16), gate.numel(),
                                   _dev(out, "out", _BF16), _stream(stream))
     _check(st, "qhead_silu_mul_bf16")
@@ -238,6 +277,8 @@ def quant_act_silu_e4m3(gate, up, hidden=None, xq=None, xscale=None, stream=None
         xq = torch.empty((rows, hidden), dtype=torch.uint8, device=gate.device)
     if xscale is None:
         xscale = torch.empty((rows,), dtype=torch.float32, device=gate.device)
+    _shape(xq, "xq", (rows, hidden))
+    _shape(xscale, "xscale", (rows,))
     st = _lib.qhead_quant_act_silu_e4m3(_dev(gate, "gate", _BF16), _dev(up, "up", _BF16), ld,
                                         rows, hidden, _dev(xq, "xq", _U8),
                                         _dev(xscale, "xscale", _F32), _stream(stream))
@@ -248,11 +289,14 @@ def quant_act_silu_e4m3(gate, up, hidden=None, xq=None, xscale=None, stream=None
 def w8a8_silu(w, row_scale, gate, up, out=None, workspace=None, stream=None) -> torch.Tensor:
     """W8A8 down projection of bf16(silu(gate) * up): w [n_out, k] E4M3 with
     per-row scales, gate/up [rows, ld] BF16 (ld >= k); out [rows, n_out]."""
+    _shape(w, "w", (None, None))
     vocab, hidden = w.shape
+    _shape(row_scale, "row_scale", (vocab,))
     rows, ld, _ = _silu_shapes(gate, up, hidden)
     out = _out(out, rows, vocab, w.device)
     if workspace is None:
         workspace = w8a8_workspace(hidden, w.device)
+    _min_numel(workspace, "workspace", w8a8_workspace_bytes(hidden))
     st = _lib.qhead_w8a8_silu(_dev(w, "w", _U8), _dev(row_scale, "row_scale", _F32),
                               _dev(gate, "gate", _BF16), _dev(up, "up", _BF16), ld, rows, hidden,
                               vocab, _dev(out, "out", _BF16), _dev(workspace, "workspace", _U8),
@@ -263,8 +307,11 @@ def w8a8_silu(w, row_scale, gate, up, out=None, workspace=None, stream=None) -> 
 
 def nvfp4(w_packed, block_scale, x, global_scale: float, out=None, stream=None) -> torch.Tensor:
     """NVFP4 W4A16 logits; w_packed [vocab, hidden/2], block_scale [vocab, hidden/16]."""
+    _shape(w_packed, "w_packed", (None, None))
     vocab = w_packed.shape[0]
     hidden = w_packed.shape[1] * 2
+    _shape(block_scale, "block_scale", (vocab, hidden // 16))
+    _shape(x, "x", (None, hidden))
     rows = x.shape[0]
     out = _out(out, rows, vocab, w_packed.device)
     st = _lib.qhead_nvfp4(_dev(w_packed, "w_packed", _U8), _dev(block_scale, "block_scale", _U8),
@@ -276,9 +323,11 @@ def nvfp4(w_packed, block_scale, x, global_scale: float, out=None, stream=None) 
 
 def quant_q8_1(x, q8=None, stream=None) -> torch.Tensor:
     """block_q8_1 activations: uint8 [rows, hidden/32*36]."""
+    _shape(x, "x", (None, None))
     rows, hidden = x.shape
     if q8 is None:
         q8 = torch.empty((rows, hidden // 32 * Q8_BLOCK_BYTES), dtype=torch.uint8, device=x.device)
+    _min_numel(q8, "q8", rows * (hidden // 32) * Q8_BLOCK_BYTES)
     st = _lib.qhead_quant_q8_1(_dev(x, "x", _BF16), rows, hidden, _dev(q8, "q8", _U8),
                                _stream(stream))
     _check(st, "qhead_quant_q8_1")
@@ -290,7 +339,9 @@ def q6k_workspace_bytes(hidden: int) -> int:
 
 
 def q6k_gemv(blocks, q8, hidden: int, out=None, stream=None) -> torch.Tensor:
+    _shape(blocks, "blocks", (None, hidden // 256 * Q6K_BLOCK_BYTES))
     vocab = blocks.shape[0]
+    _shape(q8, "q8", (None, hidden // 32 * Q8_BLOCK_BYTES))
     rows = q8.shape[0]
     out = _out(out, rows, vocab, blocks.device)
     st = _lib.qhead_q6k_gemv(_dev(blocks, "blocks", _U8), _dev(q8, "q8", _U8), rows, hidden, vocab,
@@ -301,8 +352,10 @@ def q6k_gemv(blocks, q8, hidden: int, out=None, stream=None) -> torch.Tensor:
 
 def q6k(blocks, x, out=None, workspace=None, stream=None) -> torch.Tensor:
     """Q6_K logits: x quantized to q8_1 per <= 8-row chunk, then the Q6_K GEMV."""
-    vocab = blocks.shape[0]
+    _shape(x, "x", (None, None))
     rows, hidden = x.shape
+    _shape(blocks, "blocks", (None, hidden // 256 * Q6K_BLOCK_BYTES))
+    vocab = blocks.shape[0]
     out = _out(out, rows, vocab, blocks.device)
     if workspace is None:
         workspace = torch.empty((q6k_workspace_bytes(hidden),), dtype=torch.uint8,
@@ -323,8 +376,10 @@ def q6k_static_scratch(blocks, x, out=None, stream=None) -> torch.Tensor:
     per-GPU device array instead of a workspace (nothing is allocated by the
     call except `out` when it is not given). Calls that may overlap on one GPU
     race on that array."""
-    vocab = blocks.shape[0]
+    _shape(x, "x", (None, None))
     rows, hidden = x.shape
+    _shape(blocks, "blocks", (None, hidden // 256 * Q6K_BLOCK_BYTES))
+    vocab = blocks.shape[0]
     out = _out(out, rows, vocab, blocks.device)
     st = _lib.qhead_q6k_static_scratch(_dev(blocks, "blocks", _U8), None, _dev(x, "x", _BF16),
                                        rows, hidden, vocab, _dev(out, "out", _BF16),
@@ -335,11 +390,14 @@ def q6k_static_scratch(blocks, x, out=None, stream=None) -> torch.Tensor:
 
 def quantize_fp8_rows(w_f32: torch.Tensor, codes=None, scales=None, stream=None):
     """Load-time per-row E4M3 quantization of F32 weights: (codes uint8, row scales f32)."""
+    _shape(w_f32, "w_f32", (None, None))
     vocab, hidden = w_f32.shape
     if codes is None:
         codes = torch.empty((vocab, hidden), dtype=torch.uint8, device=w_f32.device)
     if scales is None:
         scales = torch.empty((vocab,), dtype=torch.float32, device=w_f32.device)
+    _shape(codes, "codes", (vocab, hidden))
+    _shape(scales, "scales", (vocab,))
     st = _lib.qhead_quantize_fp8_rows(_dev(w_f32, "w_f32", _F32), vocab, hidden,
                                       _dev(codes, "codes", _U8), _dev(scales, "scales", _F32),
                                       _stream(stream))
@@ -351,11 +409,14 @@ def quantize_nvfp4_rows(w_f32: torch.Tensor, global_scale: float, w_packed=None,
                         block_scale=None, stream=None):
     """Load-time NVFP4 quantization of F32 weights with global multiplier g:
     (w_packed uint8 [vocab, hidden/2], block_scale uint8 [vocab, hidden/16])."""
+    _shape(w_f32, "w_f32", (None, None))
     vocab, hidden = w_f32.shape
     if w_packed is None:
         w_packed = torch.empty((vocab, hidden // 2), dtype=torch.uint8, device=w_f32.device)
     if block_scale is None:
         block_scale = torch.empty((vocab, hidden // 16), dtype=torch.uint8, device=w_f32.device)
+    _shape(w_packed, "w_packed", (vocab, hidden // 2))
+    _shape(block_scale, "block_scale", (vocab, hidden // 16))
     st = _lib.qhead_quantize_nvfp4_rows(_dev(w_f32, "w_f32", _F32), vocab, hidden,
                                         float(global_scale), _dev(w_packed, "w_packed", _U8),
                                         _dev(block_scale, "block_scale", _U8), _stream(stream))
@@ -365,10 +426,12 @@ def quantize_nvfp4_rows(w_f32: torch.Tensor, global_scale: float, w_packed=None,
 
 def quantize_q6k_rows(w_f32: torch.Tensor, blocks=None, stream=None) -> torch.Tensor:
     """Load-time Q6_K quantization of F32 weights: uint8 [vocab, hidden/256*210]."""
+    _shape(w_f32, "w_f32", (None, None))
     vocab, hidden = w_f32.shape
     if blocks is None:
         blocks = torch.empty((vocab, hidden // 256 * Q6K_BLOCK_BYTES), dtype=torch.uint8,
                              device=w_f32.device)
+    _shape(blocks, "blocks", (vocab, hidden // 256 * Q6K_BLOCK_BYTES))
     st = _lib.qhead_quantize_q6k_rows(_dev(w_f32, "w_f32", _F32), vocab, hidden,
                                       _dev(blocks, "blocks", _U8), _stream(stream))
     _check(st, "qhead_quantize_q6k_rows")
@@ -378,10 +441,13 @@ def quantize_q6k_rows(w_f32: torch.Tensor, blocks=None, stream=None) -> torch.Te
 def dequant_nvfp4_bf16(w_packed, block_scale, global_scale: float, out=None,
                        stream=None) -> torch.Tensor:
     """Load-time NVFP4 -> BF16: bf16 [rows, cols] from w_packed [rows, cols/2]."""
+    _shape(w_packed, "w_packed", (None, None))
     rows = w_packed.shape[0]
     cols = w_packed.shape[1] * 2
+    _shape(block_scale, "block_scale", (rows, cols // 16))
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.bfloat16, device=w_packed.device)
+    _shape(out, "out", (rows, cols))
     st = _lib.qhead_dequant_nvfp4_bf16(_dev(w_packed, "w_packed", _U8),
                                        _dev(block_scale, "block_scale", _U8), rows, cols,
                                        float(global_scale), _dev(out, "out", _BF16),
@@ -396,6 +462,8 @@ def dequant_fp4_e8m0_bf16(w_packed, scale_e8m0, out=None, stream=None) -> torch.
     total = w_packed.numel() * 2
     if out is None:
         out = torch.empty((total,), dtype=torch.bfloat16, device=w_packed.device)
+    if out.numel() != total:
+        raise ValueError(f"out has {out.numel()} elements, expected {total}")
     st = _lib.qhead_dequant_fp4_e8m0_bf16(_dev(w_packed, "w_packed", _U8),
                                           _dev(scale_e8m0, "scale_e8m0", _U8), total,
                                           scale_e8m0.numel(), _dev(out, "out", _BF16),

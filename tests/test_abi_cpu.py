@@ -247,3 +247,62 @@ def test_binding_rejects_host_tensors(qh):
     w = torch.zeros((8, 16), dtype=torch.uint8)
     with pytest.raises(ValueError):
         qh.fp8_rowscale(w, torch.zeros(8), torch.zeros((1, 16), dtype=torch.bfloat16))
+
+
+def test_binding_rejects_wrong_shapes(qh):
+    """Every wrapper checks its tensors' shapes before any pointer reaches the
+    library (the library reads and writes by the sizes passed, so a short
+    tensor would be overrun). Host tensors serve here: the shape check comes
+    before the device check, and the message names the shape."""
+    import torch
+
+    u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+    V, H, R = 8, 512, 2
+    w = torch.zeros((V, H), dtype=u8)
+    s = torch.zeros(V, dtype=f32)
+    x = torch.zeros((R, H), dtype=bf)
+    xq = torch.zeros((R, H), dtype=u8)
+    sa = torch.zeros(R, dtype=f32)
+    shape_msg = r"shape|elements|exceeds"
+    cases = [
+        lambda: qh.fp8_rowscale(w, s[:V - 1], x),
+        lambda: qh.fp8_rowscale(w, s, x[:, :H - 16]),
+        lambda: qh.fp8_rowscale(w, s, x, out=torch.zeros((R, V - 1), dtype=bf)),
+        lambda: qh.fp8_rowscale(w, s, x, out=torch.zeros((R + 1, V), dtype=bf)),
+        lambda: qh.quant_act_e4m3(x, xq=xq[:1]),
+        lambda: qh.quant_act_e4m3(x, xscale=sa[:1]),
+        lambda: qh.w8a8_gemv(w, s, xq, sa[:1]),
+        lambda: qh.w8a8_gemv(w, s, xq[:, :H - 32], sa),
+        lambda: qh.w8a8(w, s, x, workspace=torch.zeros(4, dtype=u8)),
+        lambda: qh.w8a8_silu(w, s, x, x[:, :H - 16]),
+        lambda: qh.quant_act_silu_e4m3(x, x, hidden=H + 16),
+        lambda: qh.silu_mul_bf16(x, x, out=torch.zeros((R, H - 1), dtype=bf)),
+        lambda: qh.nvfp4(torch.zeros((V, H // 2), dtype=u8), torch.zeros((V, H // 32), dtype=u8),
+                         x, 1.0),
+        lambda: qh.nvfp4(torch.zeros((V, H // 2), dtype=u8), torch.zeros((V, H // 16), dtype=u8),
+                         x[:, :H // 2], 1.0),
+        lambda: qh.quant_q8_1(x, q8=torch.zeros(R * (H // 32) * 36 - 1, dtype=u8)),
+        lambda: qh.q6k_gemv(torch.zeros((V, 2 * 210), dtype=u8),
+                            torch.zeros((R, H // 32 * 36), dtype=u8), H + 256),
+        lambda: qh.q6k_gemv(torch.zeros((V, 2 * 210), dtype=u8),
+                            torch.zeros((R, H // 32 * 36 - 36), dtype=u8), H),
+        lambda: qh.q6k(torch.zeros((V, 3 * 210), dtype=u8), x),
+        lambda: qh.q6k_static_scratch(torch.zeros((V, 1 * 210), dtype=u8), x),
+        lambda: qh.quantize_fp8_rows(torch.zeros((V, H)), codes=w[:, :H - 1]),
+        lambda: qh.quantize_fp8_rows(torch.zeros((V, H)), scales=s[:1]),
+        lambda: qh.quantize_nvfp4_rows(torch.zeros((V, H)), 1.0,
+                                       block_scale=torch.zeros((V, H // 8), dtype=u8)),
+        lambda: qh.quantize_q6k_rows(torch.zeros((V, H)),
+                                     blocks=torch.zeros((V, 210), dtype=u8)),
+        lambda: qh.dequant_nvfp4_bf16(torch.zeros((V, H // 2), dtype=u8),
+                                      torch.zeros((V, H // 16 - 1), dtype=u8), 1.0),
+        lambda: qh.dequant_fp4_e8m0_bf16(torch.zeros(H // 2, dtype=u8),
+                                         torch.zeros(H // 32, dtype=u8),
+                                         out=torch.zeros(H - 2, dtype=bf)),
+    ]
+    for call in cases:
+        with pytest.raises(ValueError, match=shape_msg):
+            call()
+    # the same call with matching shapes gets as far as the device check
+    with pytest.raises(ValueError, match="device|CUDA|cuda"):
+        qh.fp8_rowscale(w, s, x)
