@@ -78,6 +78,7 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float t) {
 
 // DPP controls (gfx9 encoding).
 constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowMirror = 0x140;
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]

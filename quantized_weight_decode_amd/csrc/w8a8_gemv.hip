@@ -109,6 +109,79 @@ __device__ __forceinline__ void stage_codes_bf16(uint4* xs, const uint8_t* xq, i
     }
 }
 
+// The dot2 steps of one 16-k granule of every chain a lane holds: for each
+// row r and vocab row t, acc[r * T + t] takes the 8 pairs of wb[t] times the
+// activation pairs of row r (two 16-byte LDS words at xlo + r * RS for rows
+// 0..7, xhi + (r - 8) * RS above), in pair order.
+template <int R, int T, int RS, int NP>
+__device__ __forceinline__ void granule_dots(float (&acc)[NP], const uint32_t (&wb)[T][8],
+                                             const uint4* xlo, const uint4* xhi) {
+    if constexpr (R >= 4) {
+        // Rows in groups of G: for each pair p the G * T chains of a group
+        // take their dot2 one after the other (independent chains keep the
+        // VALU issuing); each chain still adds its pairs in k order. The next
+        // group's activations are read while this one is computed.
+        constexpr int G = T >= 4 ? 4 : 2;
+        uint32_t xg[2][G][8];
+        auto read_group = [&](int rg, uint32_t(&dst)[G][8]) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (rg + g < R) {
+                    const uint4* xp = (rg + g) < 8 ? xlo + (rg + g) * RS : xhi + (rg + g - 8) * RS;
+                    const uint4 xa = xp[0];
+                    const uint4 xb = xp[1];
+                    dst[g][0] = xa.x; dst[g][1] = xa.y; dst[g][2] = xa.z;
+                    dst[g][3] = xa.w; dst[g][4] = xb.x; dst[g][5] = xb.y;
+                    dst[g][6] = xb.z; dst[g][7] = xb.w;
+                }
+            }
+        };
+        read_group(0, xg[0]);
+#pragma unroll
+        for (int rg = 0; rg < R; rg += G) {
+            if (rg + G < R) read_group(rg + G, xg[((rg / G) + 1) & 1]);
+            const int cb = (rg / G) & 1;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    if (rg + g < R) {
+#pragma unroll
+                        for (int t = 0; t < T; ++t)
+                            acc[(rg + g) * T + t] =
+                                dot2_bf16(xg[cb][g][p], wb[t][p], acc[(rg + g) * T + t]);
+                    }
+                }
+            }
+        }
+    } else {
+        constexpr int LA = R < 2 ? R : 2;
+        constexpr int NBUF = LA + 1;
+        uint4 xr[NBUF][2];
+#pragma unroll
+        for (int r = 0; r < LA; ++r) {
+            xr[r][0] = xlo[r * RS];
+            xr[r][1] = xlo[r * RS + 1];
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (r + LA < R) {
+                xr[(r + LA) % NBUF][0] = xlo[(r + LA) * RS];
+                xr[(r + LA) % NBUF][1] = xlo[(r + LA) * RS + 1];
+            }
+            const uint4 xa = xr[r % NBUF][0], xb = xr[r % NBUF][1];
+            const uint32_t xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                float a = acc[r * T + t];
+#pragma unroll
+                for (int p = 0; p < 8; ++p) a = dot2_bf16(xv[p], wb[t][p], a);
+                acc[r * T + t] = a;
+            }
+        }
+    }
+}
+
 // Lanes: chain c = lane bits {0, 1, 3}, vocab slot o = lane bits {2, 4, 5};
 // a band is 8 slots x T consecutive vocab rows. An item is (band, 128-k
 // step): lane (c, o) loads the 16 weight bytes of granule c of the step for
@@ -212,73 +285,7 @@ w8a8_valu_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
 #pragma unroll
                 for (int t = 0; t < T; ++t) e4m3x16_to_bf16(cur[t], wb[t]);
                 const uint4* xrow = xs + s * (kStepK / 8) + 2 * c;
-                const uint4* xrow_hi = xrow + hi_rows;
-                if constexpr (R >= 4) {
-                    // Rows in groups of G: for each pair p the G * T chains of
-                    // a group take their dot2 one after the other (independent
-                    // chains keep the VALU issuing); each chain still adds its
-                    // pairs in k order. The next group's activations are read
-                    // while this one is computed.
-                    constexpr int G = T >= 4 ? 4 : 2;
-                    uint32_t xg[2][G][8];
-                    auto read_group = [&](int rg, uint32_t(&dst)[G][8]) {
-#pragma unroll
-                        for (int g = 0; g < G; ++g) {
-                            if (rg + g < R) {
-                                const uint4* xp = (rg + g) < 8 ? xrow + (rg + g) * kTileVec
-                                                               : xrow_hi + (rg + g - 8) * kTileVec;
-                                const uint4 xa = xp[0];
-                                const uint4 xb = xp[1];
-                                dst[g][0] = xa.x; dst[g][1] = xa.y; dst[g][2] = xa.z;
-                                dst[g][3] = xa.w; dst[g][4] = xb.x; dst[g][5] = xb.y;
-                                dst[g][6] = xb.z; dst[g][7] = xb.w;
-                            }
-                        }
-                    };
-                    read_group(0, xg[0]);
-#pragma unroll
-                    for (int rg = 0; rg < R; rg += G) {
-                        if (rg + G < R) read_group(rg + G, xg[((rg / G) + 1) & 1]);
-                        const int cb = (rg / G) & 1;
-#pragma unroll
-                        for (int p = 0; p < 8; ++p) {
-#pragma unroll
-                            for (int g = 0; g < G; ++g) {
-                                if (rg + g < R) {
-#pragma unroll
-                                    for (int t = 0; t < T; ++t)
-                                        acc[(rg + g) * T + t] =
-                                            dot2_bf16(xg[cb][g][p], wb[t][p], acc[(rg + g) * T + t]);
-                                }
-                            }
-                        }
-                    }
-                } else {
-                    constexpr int LA = R < 2 ? R : 2;
-                    constexpr int NBUF = LA + 1;
-                    uint4 xr[NBUF][2];
-#pragma unroll
-                    for (int r = 0; r < LA; ++r) {
-                        xr[r][0] = xrow[r * kTileVec];
-                        xr[r][1] = xrow[r * kTileVec + 1];
-                    }
-#pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        if (r + LA < R) {
-                            xr[(r + LA) % NBUF][0] = xrow[(r + LA) * kTileVec];
-                            xr[(r + LA) % NBUF][1] = xrow[(r + LA) * kTileVec + 1];
-                        }
-                        const uint4 xa = xr[r % NBUF][0], xb = xr[r % NBUF][1];
-                        const uint32_t xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-#pragma unroll
-                        for (int t = 0; t < T; ++t) {
-                            float a = acc[r * T + t];
-#pragma unroll
-                            for (int p = 0; p < 8; ++p) a = dot2_bf16(xv[p], wb[t][p], a);
-                            acc[r * T + t] = a;
-                        }
-                    }
-                }
+                granule_dots<R, T, kTileVec>(acc, wb, xrow, xrow + hi_rows);
                 if (s + 1 == nstep) {
                     dpp_level<kDppQuadXor1, 1, NP>(acc, lane);
                     dpp_level<kDppQuadXor2, 2, NP1>(prefix<NP1>(acc), lane);
@@ -336,6 +343,229 @@ hipError_t launch_valu(const uint8_t* W, const float* ws, const uint8_t* xq, con
     const int nsuper = (int)((per_wave + MAXB - 1) / MAXB);
     hipLaunchKernelGGL((w8a8_valu_kernel<R, T, WAVES, MAXB, BPC>), dim3((unsigned)blocks),
                        dim3(WAVES * kWave), 0, stream, W, ws, xq, xs, H, V, out, nsuper);
+    return hipGetLastError();
+}
+
+// ----------------------------------------------- split VALU kernel (narrow V)
+
+// A projection with few output rows (a few thousand, as in an FFN down
+// projection) gives the kernel above too few bands, and so too few waves, to
+// keep the weight stream busy. Here the KS waves of a workgroup share one band
+// (8 slots x T vocab rows, the same lanes as above) and split the hidden
+// dimension by 4096-k tile: wave w takes tiles w, w + KS, ... Each wave walks
+// its items (tile, 128-k step) through a ring of PF loads in flight; an item
+// holds the T weight granules of the lane and the step's activation codes (a
+// lane of row a = lane / 8 (+ 8) and chain lane % 8 loads that granule), which
+// the wave converts into a private LDS window before its lanes read the pairs
+// of their chain. There is no barrier until the band ends: every wave leaves
+// its tile sums (after the same tree as above) in LDS, and wave 0 adds them in
+// tile order. Chains, pair order, tree and tile order equal the kernel above,
+// so the logits carry the same bits.
+template <int R, int T, int PF>
+__global__ void __launch_bounds__(8 * kWave)
+w8a8_valu_split_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
+                       const uint8_t* __restrict__ xq, const float* __restrict__ xscale, int H,
+                       int V, uint16_t* __restrict__ out, int nbw) {
+    constexpr int N = T * R;
+    constexpr int NP = next_pow2(N);
+    constexpr int NP1 = half_or_one(NP);
+    constexpr int NP2 = half_or_one(NP1);
+    constexpr int NQ = half_or_one(NP2);
+    constexpr int BAND = 8 * T;
+    constexpr int NA = (R + 7) / 8;               // activation loads per lane per item
+    constexpr int WIN = R * kChains * 2;          // uint4 per wave window (one step)
+    constexpr int kStepsPerTile = kW8TileK / kStepK;
+    static_assert(NP <= 64, "T*R must be <= 64");
+    static_assert(PF >= 2, "ring of at least two items");
+    extern __shared__ uint4 lds_dyn[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int KS = blockDim.x >> 6;
+    const int c = (lane & 3) | ((lane >> 1) & 4);
+    const int o = ((lane >> 2) & 1) | ((lane >> 3) & 6);
+    const int NB = (V + BAND - 1) / BAND;
+    const int NT = (H + kW8TileK - 1) / kW8TileK;
+    const int last_steps = (H - (NT - 1) * kW8TileK + kStepK - 1) / kStepK;
+    // this wave's tiles: wave, wave + KS, ... (the launch keeps KS <= NT)
+    const int nq = (NT - wave + KS - 1) / KS;
+    const bool owns_last = (NT - 1 - wave) % KS == 0;
+    const int ipb = nq * kStepsPerTile - (owns_last ? kStepsPerTile - last_steps : 0);
+    const int total = nbw * ipb;
+
+    uint4* win = lds_dyn + wave * WIN;
+    float* tsum = reinterpret_cast<float*>(lds_dyn + KS * WIN);
+
+    int idx0 = 0;
+    bool writer = true;
+    {
+        int n = NP;
+        const int bits[3] = {lane & 1, (lane >> 1) & 1, (lane >> 3) & 1};
+#pragma unroll
+        for (int lv = 0; lv < 3; ++lv) {
+            if (n >= 2) {
+                n /= 2;
+                idx0 += bits[lv] * n;
+            } else if (bits[lv]) {
+                writer = false;
+            }
+        }
+    }
+
+    // Item positions: band j of this workgroup, tile q of this wave, step s.
+    struct Pos {
+        int j, q, s;
+    };
+    auto steps_of = [&](int q) { return (q == nq - 1 && owns_last) ? last_steps : kStepsPerTile; };
+    auto advance = [&](Pos& p) {
+        if (++p.s == steps_of(p.q)) {
+            p.s = 0;
+            if (++p.q == nq) {
+                p.q = 0;
+                ++p.j;
+            }
+        }
+    };
+    // Unconditional loads: past the hidden tail a lane re-reads the row's
+    // last 16 bytes (its activations are zero), past the vocab tail the last
+    // row (never stored), past the last band of the grid the last row.
+    auto load_item = [&](const Pos& p, uint4(&wd)[T], uint4(&ad)[NA]) __attribute__((always_inline)) {
+        const int band = blockIdx.x + p.j * gridDim.x;
+        const int kb = (wave + KS * p.q) * kW8TileK + p.s * kStepK;
+        const int k = min(kb + c * kGranK, H - 16);
+        const int v0 = band * BAND + o * T;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int v = min(v0 + t, V - 1);
+            wd[t] = load_stream16(W + (size_t)v * H + k);
+        }
+        const int ka = min(kb + (lane & 7) * kGranK, H - 16);
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            const int r = min((lane >> 3) + 8 * a, R - 1);
+            ad[a] = *reinterpret_cast<const uint4*>(xq + (size_t)r * H + ka);
+        }
+    };
+
+    uint4 wring[PF][T];
+    uint4 aring[PF][NA];
+    float acc[NP];
+    float part[NQ];
+    Pos cur{0, 0, 0};
+    Pos pf{0, 0, 0};
+    int pf_it = 0;
+#pragma unroll
+    for (int i = 0; i + 1 < PF; ++i) {
+        load_item(pf, wring[i], aring[i]);
+        if (pf_it + 1 < total) {
+            advance(pf);
+            ++pf_it;
+        }
+    }
+
+    auto item = [&](auto sl_tag) __attribute__((always_inline)) {
+        constexpr int SL = decltype(sl_tag)::value;
+        load_item(pf, wring[(SL + PF - 1) % PF], aring[(SL + PF - 1) % PF]);
+        if (pf_it + 1 < total) {
+            advance(pf);
+            ++pf_it;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (cur.s == 0) {
+#pragma unroll
+            for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
+        }
+        const int tt = wave + KS * cur.q;
+        const int kb = tt * kW8TileK + cur.s * kStepK;
+        // this step's activations into the window: [row][chain] x 2 uint4
+        {
+            const bool kin = kb + (lane & 7) * kGranK < H;
+#pragma unroll
+            for (int a = 0; a < NA; ++a) {
+                const int r = (lane >> 3) + 8 * a;
+                if (r < R) {
+                    uint32_t pr[8];
+                    e4m3x16_to_bf16(aring[SL][a], pr);
+                    uint4* dst = win + (r * kChains + (lane & 7)) * 2;
+                    dst[0] = kin ? make_uint4(pr[0], pr[1], pr[2], pr[3]) : make_uint4(0, 0, 0, 0);
+                    dst[1] = kin ? make_uint4(pr[4], pr[5], pr[6], pr[7]) : make_uint4(0, 0, 0, 0);
+                }
+            }
+        }
+        uint32_t wb[T][8];
+#pragma unroll
+        for (int t = 0; t < T; ++t) e4m3x16_to_bf16(wring[SL][t], wb[t]);
+        // the window's writes come before its reads (a wave's LDS accesses
+        // run in order; this keeps the compiler from moving the reads up)
+        asm volatile("" ::: "memory");
+        const uint4* xrow = win + 2 * c;
+        granule_dots<R, T, kChains * 2>(acc, wb, xrow, xrow + 8 * kChains * 2);
+        asm volatile("" ::: "memory");
+        if (cur.s + 1 == steps_of(cur.q)) {
+            dpp_level<kDppQuadXor1, 1, NP>(acc, lane);
+            dpp_level<kDppQuadXor2, 2, NP1>(prefix<NP1>(acc), lane);
+            dpp_level<kDppRowRor8, 8, NP2>(prefix<NP2>(acc), lane);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) tsum[(tt * NQ + q) * kWave + lane] = acc[q];
+            if (cur.q == nq - 1) {
+                // end of the band: its tile sums in tile order, by wave 0
+                __syncthreads();
+                const int band = blockIdx.x + cur.j * gridDim.x;
+                if (wave == 0) {
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) part[q] = tsum[q * kWave + lane];
+                    for (int t2 = 1; t2 < NT; ++t2)
+#pragma unroll
+                        for (int q = 0; q < NQ; ++q)
+                            part[q] = part[q] + tsum[(t2 * NQ + q) * kWave + lane];
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) {
+                        const int idx = idx0 + q;
+                        const int r = idx / T;
+                        const int t = idx - r * T;
+                        const int v = band * BAND + o * T + t;
+                        if (writer && idx < N && band < NB && v < V) {
+                            const float y = (part[q] * xscale[r]) * wscale[v];
+                            out[(size_t)r * V + v] = f32_to_bf16_rne(y);
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        advance(cur);
+    };
+
+    int it = 0;
+#pragma unroll 1
+    for (; it + PF <= total; it += PF)
+        static_for<PF>([&](auto sl) __attribute__((always_inline)) { item(sl); });
+    static_for<PF>([&](auto sl) __attribute__((always_inline)) {
+        if (it + decltype(sl)::value < total) item(sl);
+    });
+}
+
+// LDS bytes of the split kernel: KS windows, then NT x NQ x 64 tile sums.
+template <int R, int T>
+constexpr size_t split_lds_bytes(int KS, int NT) {
+    constexpr int NQ = half_or_one(half_or_one(half_or_one(next_pow2(T * R))));
+    return (size_t)KS * R * kChains * 2 * 16 + (size_t)NT * NQ * kWave * 4;
+}
+
+template <int R, int T, int PF>
+hipError_t launch_valu_split(const uint8_t* W, const float* ws, const uint8_t* xq, const float* xs,
+                             int H, int V, uint16_t* out, const DeviceInfo& dev,
+                             hipStream_t stream) {
+    const int NT = (H + kW8TileK - 1) / kW8TileK;
+    const int KS = NT < 8 ? NT : 8;
+    const int64_t NB = (V + 8 * T - 1) / (8 * T);
+    int64_t blocks = NB;
+    const int64_t cap = (int64_t)dev.num_cus * 16;
+    if (blocks > cap) blocks = cap;
+    const int nbw = (int)((NB + blocks - 1) / blocks);
+    const size_t lds = split_lds_bytes<R, T>(KS, NT);
+    hipLaunchKernelGGL((w8a8_valu_split_kernel<R, T, PF>), dim3((unsigned)blocks),
+                       dim3(KS * kWave), lds, stream, W, ws, xq, xs, H, V, out, nbw);
     return hipGetLastError();
 }
 
@@ -653,6 +883,38 @@ hipError_t launch_mfma(const uint8_t* W, const float* ws, const uint8_t* xq, con
 hipError_t run_w8a8_gemv(const uint8_t* W, const float* sw, const uint8_t* xq, const float* sa,
                          int R, int H, int V, uint16_t* out, const DeviceInfo& dev,
                          hipStream_t stream) {
+    // Narrow projections (fewer than two bands of the kernel below per SIMD)
+    // split the hidden dimension over the waves of a workgroup instead, when
+    // its LDS (windows and tile sums) stays within 64 KiB.
+    const int T_main = R <= 4 ? 2 : 4;
+    const int64_t bands_main = (V + 8 * T_main - 1) / (8 * T_main);
+    const int NT = (H + kW8TileK - 1) / kW8TileK;
+    if (R >= 1 && R < 16 && bands_main < (int64_t)dev.num_cus * 8 &&
+        split_lds_bytes<15, 4>(NT < 8 ? NT : 8, NT) <= 65536) {
+        switch (R) {
+#define QH_W8_SPLIT(RR)   \
+    case RR:              \
+        return launch_valu_split<RR, 4, 4>(W, sw, xq, sa, H, V, out, dev, stream);
+            QH_W8_SPLIT(1)
+            QH_W8_SPLIT(2)
+            QH_W8_SPLIT(3)
+            QH_W8_SPLIT(4)
+            QH_W8_SPLIT(5)
+            QH_W8_SPLIT(6)
+            QH_W8_SPLIT(7)
+            QH_W8_SPLIT(8)
+            QH_W8_SPLIT(9)
+            QH_W8_SPLIT(10)
+            QH_W8_SPLIT(11)
+            QH_W8_SPLIT(12)
+            QH_W8_SPLIT(13)
+            QH_W8_SPLIT(14)
+            QH_W8_SPLIT(15)
+#undef QH_W8_SPLIT
+            default:
+                break;
+        }
+    }
     switch (R) {
 #define QH_W8_VALU(RR, TT, WV, MB, BPC)                                                   \
     case RR:                                                                              \
@@ -680,6 +942,23 @@ hipError_t run_w8a8_gemv(const uint8_t* W, const float* sw, const uint8_t* xq, c
     // Launch shapes <RT, vocab tiles per workgroup, waves per tile, weight
     // slabs in flight>, eight waves per workgroup (two per SIMD): up to 32
     // rows one wave per tile, up to 64 two, above four (2 chains each).
+    // Narrow projections (fewer than 4 vocab tiles per CU) take two tiles of
+    // four waves per workgroup at every row count, for more workgroups.
+    const int64_t ntiles = (V + 15) / 16;
+    if (ntiles < (int64_t)dev.num_cus * 4) {
+        switch ((R + 15) / 16) {
+            case 1:
+                return launch_mfma<1, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            case 2:
+                return launch_mfma<2, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            case 3:
+                return launch_mfma<3, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            case 4:
+                return launch_mfma<4, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            default:
+                break;
+        }
+    }
     switch ((R + 15) / 16) {
         case 1:
             return launch_mfma<1, 8, 1, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);

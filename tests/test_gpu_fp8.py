@@ -136,12 +136,19 @@ def test_fp8_edge_shapes(qh):
 
 
 def test_fp8_rows_zero_is_noop(qh):
+    """rows = 0 through the C ABI: success, and the output buffer (here one
+    row long) is left untouched."""
     w, s = _fp8_small(64, 64)
+    wd, sd = dev_u8(w), dev_f32(s)
+    x = torch.zeros((1, 64), dtype=torch.bfloat16, device=DEV)
     out = torch.full((1, 64), 7.0, dtype=torch.bfloat16, device=DEV)
-    qh.fp8_rowscale(dev_u8(w), dev_f32(s), torch.empty((0, 64), dtype=torch.bfloat16, device=DEV),
-                    out=out)
+    st = qh.lib().qhead_fp8_rowscale(wd.data_ptr(), sd.data_ptr(), x.data_ptr(), 0, 64, 64,
+                                     out.data_ptr(), torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
+    assert st == 0
     assert torch.all(out == 7.0)
+    # the binding passes rows = 0 for an empty x and returns an empty result
+    assert qh.fp8_rowscale(wd, sd, x[:0]).shape == (0, 64)
 
 
 def test_fp8_zero_rows_and_scale(qh):

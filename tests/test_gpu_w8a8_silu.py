@@ -97,6 +97,46 @@ def test_quant_act_silu_bit_exact(qh, rows, hidden, ld):
     assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:5].tolist()} (ambiguous: {amb})"
 
 
+def test_quant_act_silu_row_max_edges(qh):
+    """Rows that stress how the quantizer finds the row maximum (a cheap
+    screen of every product, then exact products only for the candidates):
+    the maximum held by one element with a very negative gate and a huge up
+    (silu(g) below 2^-100, so it is never screened), by an element with
+    silu(g) ~ 5e-25, by the only product above 2^-100 in a row of products
+    below it, products all within 2^-6 of each other (every one a candidate),
+    a row of zeros with one tiny product, and a row of zeros with one
+    negative zero. Scales and codes bit-exact."""
+    H = 4096
+    rng = np.random.Generator(np.random.PCG64(404))
+    rows = 8
+    g = _bits(rng.normal(0.0, 1.0, (rows, H)))
+    u = _bits(rng.normal(0.0, 1e-6, (rows, H)))
+    g[0, 777], u[0, 777] = _bits([-90.0])[0], _bits([1e38])[0]
+    g[1, 5], u[1, 5] = _bits([-60.0])[0], _bits([1e20])[0]
+    g[2, :] = _bits(np.full(H, 1e-20))
+    u[2, :] = _bits(rng.uniform(-1e-12, 1e-12, H))
+    g[2, 4000], u[2, 4000] = _bits([1e-15])[0], _bits([1e-15])[0]
+    g[3, :] = _bits(np.full(H, 2.0))
+    u[3, :] = _bits(1.0 - rng.integers(0, 4, H) * 2.0 ** -8)
+    g[4, :] = 0
+    u[4, :] = _bits(rng.normal(0.0, 1.0, H))
+    g[4, 123], u[4, 123] = _bits([1e-25])[0], _bits([-1e-20])[0]
+    g[5, :] = 0
+    g[5, 9], u[5, 9] = 0x8000, 0x3F80
+    g[6, ::2] = _bits(np.full(H // 2, -100.0))   # silu(g) ~ -4e-42
+    u[6, ::2] = _bits(np.full(H // 2, 3e38))
+    g[7, :] = _bits(rng.normal(0.0, 1.0, H))
+    u[7, :] = _bits(np.full(H, 1.0))
+    xq, sa = qh.quant_act_silu_e4m3(dev_bf16(g), dev_bf16(u), H)
+    torch.cuda.synchronize()
+    rq, rs, amb = oracle.quant_act_silu_e4m3(g, u, H)
+    got_q, got_s = xq.cpu().numpy(), sa.cpu().numpy()
+    assert np.array_equal(got_s.view(np.uint32), rs.view(np.uint32)), \
+        f"scales differ in rows {np.nonzero(got_s.view(np.uint32) != rs.view(np.uint32))[0]}"
+    bad = np.argwhere(got_q != rq)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:5].tolist()} (ambiguous: {amb})"
+
+
 def _fp8_weights(V, H, seed):
     wf = synth.weight_rows_f32(synth.SILU_DOWN_7168X18432, 0, V, vocab=V, hidden=H)
     return oracle.prep_fp8_rows(wf)
@@ -123,6 +163,26 @@ def test_w8a8_silu_logits_and_row_invariance(qh):
     dq, ds = qh.quant_act_silu_e4m3(dev_bf16(g), dev_bf16(u), H)
     two = host_bits(qh.w8a8_gemv(wd, sd, dq, ds))
     assert np.array_equal(two, outs[130])
+
+
+def test_w8a8_silu_long_rows(qh):
+    """An FFN width past the two-launch quantizer's 64 slices of 512 columns
+    (33024 > 32768): the call quantizes in one launch instead; logits within
+    the bound and equal to quantize-then-GEMV through the separate entry
+    points."""
+    V, H = 300, 33024
+    w, s = _fp8_weights(V, H, 0)
+    wd, sd = dev_u8(w), dev_f32(s)
+    g, u = _gate_up(3, H, H, 5)
+    xq, sa, _ = oracle.quant_act_silu_e4m3(g, u, H)
+    ref, ad = oracle.w8a8_ref(w, s, xq, sa)
+    log(f"[case] w8a8_silu V={V} H={H} R=3")
+    out = host_bits(qh.w8a8_silu(wd, sd, dev_bf16(g), dev_bf16(u)))
+    torch.cuda.synchronize()
+    assert_within_bound(out, ref, ad, "w8a8_silu long rows")
+    dq, ds = qh.quant_act_silu_e4m3(dev_bf16(g), dev_bf16(u), H)
+    assert np.array_equal(dq.cpu().numpy(), xq)
+    assert np.array_equal(host_bits(qh.w8a8_gemv(wd, sd, dq, ds)), out)
 
 
 def test_w8a8_silu_full_size(qh):
@@ -153,7 +213,7 @@ def test_w8a8_silu_rejects_bad_shapes(qh):
     g = torch.zeros((2, 40), dtype=torch.bfloat16, device=DEV)  # ld 40 % 8 == 0 but hidden 32 ok
     out = qh.w8a8_silu(w, s, g, g)
     assert out.shape == (2, 64)
-    with pytest.raises(qh.QheadError):  # ld < hidden
+    with pytest.raises(ValueError):  # ld < hidden: the binding's shape check
         qh.w8a8_silu(torch.zeros((64, 48), dtype=torch.uint8, device=DEV), s, g, g)
     with pytest.raises(qh.QheadError):  # ld % 8 != 0
         g2 = torch.zeros((2, 36), dtype=torch.bfloat16, device=DEV)
