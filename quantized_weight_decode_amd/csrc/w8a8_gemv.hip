@@ -604,10 +604,13 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
     constexpr int UNITS = kChains * RP;          // (chain, row) staging units per slab
     constexpr int UPT = (UNITS + NTHREADS - 1) / NTHREADS;
     static_assert(CS == 1 || CS == 2 || CS == 4, "8 chains over 1, 2 or 4 waves");
+    static_assert(PF % 2 == 0, "the staging slots follow the slab parity");
     // the tree's exchange reuses a slab buffer: (CS - 1) partial sums per tile
     static_assert((CS - 1) * VTW * RT * kWave <= SLAB_VEC, "exchange fits a slab buffer");
     __shared__ uint4 xs[2][SLAB_VEC];
     __shared__ float xsc[RP];
+    // the tile sums so far of each vocab tile (kept by its wave h = 0)
+    __shared__ f32x4_t partl[VTW][RT][kWave];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -618,124 +621,185 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
     const int ntiles = (V + 15) / 16;
     const int NS = (H + kSlabK - 1) / kSlabK;
     const int total = nrounds * NS;
+    const int nblk = gridDim.x;
 
-    // Staging of slab `s`: unit u = (chain, row), rows fastest, so
-    // consecutive threads write consecutive 16-byte LDS words. The loads use
-    // clamped addresses and are consumed only when the slab is written
-    // (rows >= R and k >= H become zero there), so they stay in flight.
-    auto stage_load = [&](int s, uint4(&st)[UPT][2]) __attribute__((always_inline)) {
-        const int k_s = s * kSlabK;
+    // Staging: this thread's units u = threadIdx.x + j * NTHREADS = (chain X,
+    // row r), rows fastest (consecutive threads write consecutive 16-byte LDS
+    // words). Rows >= R load row R - 1 and are staged as they come: an MFMA
+    // row of A only feeds the same row of the result, and those rows are
+    // never stored. Columns k >= H are staged as zero.
+    const uint8_t* ssrc[UPT];
+    int sldo[UPT], skx[UPT];
+    bool sact[UPT];
 #pragma unroll
-        for (int j = 0; j < UPT; ++j) {
-            const int u = min((int)threadIdx.x + j * NTHREADS, UNITS - 1);
-            const int r = min(u % RP, R - 1);
-            const int X = u / RP;
+    for (int j = 0; j < UPT; ++j) {
+        const int u = (int)threadIdx.x + j * NTHREADS;
+        sact[j] = UNITS % NTHREADS == 0 || u < UNITS;
+        const int uu = min(u, UNITS - 1);
+        const int r = uu % RP;
+        const int X = uu / RP;
+        ssrc[j] = xq + (size_t)min(r, R - 1) * H;
+        sldo[j] = X * 4 * RP + r;
+        skx[j] = X * kGranK;
+    }
+    // Loads stay unconditional (clamped addresses): a load inside a branch
+    // would make the compiler wait for every load in flight.
+    auto stage_load = [&](int k_s, uint4(&st)[UPT][2]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int gb = 0; gb < 2; ++gb) {
-                const int k = min(k_s + gb * kStepK + X * kGranK, H - 16);
-                st[j][gb] = *reinterpret_cast<const uint4*>(xq + (size_t)r * H + k);
-            }
-        }
+        for (int j = 0; j < UPT; ++j)
+#pragma unroll
+            for (int gb = 0; gb < 2; ++gb)
+                st[j][gb] = *reinterpret_cast<const uint4*>(
+                    ssrc[j] + min(k_s + gb * kStepK + skx[j], H - 16));
     };
-    auto stage_write = [&](int s, const uint4(&st)[UPT][2], uint4* dst) __attribute__((always_inline)) {
-        const int k_s = s * kSlabK;
+    auto stage_write = [&](int k_s, const uint4(&st)[UPT][2], uint4* dst) __attribute__((always_inline)) {
+        const bool full = k_s + kSlabK <= H;  // uniform: no column past the end
 #pragma unroll
         for (int j = 0; j < UPT; ++j) {
-            const int u = (int)threadIdx.x + j * NTHREADS;
-            if (UNITS % NTHREADS == 0 || u < UNITS) {
-                const int r = u % RP;
-                const int X = u / RP;
+            if (sact[j]) {
                 uint32_t pa[8], pb[8];
                 e4m3x16_to_bf16(st[j][0], pa);
                 e4m3x16_to_bf16(st[j][1], pb);
-                const bool oka = r < R && k_s + X * kGranK < H;
-                const bool okb = r < R && k_s + kStepK + X * kGranK < H;
+                if (!full) {
+                    const bool oka = k_s + skx[j] < H;
+                    const bool okb = k_s + kStepK + skx[j] < H;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    pa[i] = oka ? pa[i] : 0u;
-                    pb[i] = okb ? pb[i] : 0u;
+                    for (int i = 0; i < 8; ++i) {
+                        pa[i] = oka ? pa[i] : 0u;
+                        pb[i] = okb ? pb[i] : 0u;
+                    }
                 }
 #pragma unroll
                 for (int gg = 0; gg < 4; ++gg)
-                    dst[(X * 4 + gg) * RP + r] = make_uint4(pa[gg], pa[4 + gg], pb[gg], pb[4 + gg]);
+                    dst[sldo[j] + gg * RP] = make_uint4(pa[gg], pa[4 + gg], pb[gg], pb[4 + gg]);
             }
         }
     };
-    const int nblk = gridDim.x;
-    auto tile_of = [&](int it) { return ((it / NS) * nblk + (int)blockIdx.x) * VTW + vt; };
-    // Weight loads of slab `it`. LG = 4: two loads per group of four chains
-    // (lane group g: chain g of the group; granule A, then B), a 64-byte run
-    // per row. LG = 2: one load per chain pair (lane group g: chain g/2 of
-    // the pair, granule g & 1), two 32-byte runs per row.
-    auto wload = [&](int it, uint4(&dst)[NLW]) __attribute__((always_inline)) {
-        const int k_s = (it % NS) * kSlabK;
-        const int v = min(tile_of(it) * 16 + i16, V - 1);
-        const uint8_t* wrow = W + (size_t)v * H;
+    // Weight loads of a slab of vocab tile `tile`. LG = 4: two loads per
+    // group of four chains (lane group g: chain g of the group; granule A,
+    // then B), a 64-byte run per row. LG = 2: one load per chain pair (lane
+    // group g: chain g/2 of the pair, granule g & 1), two 32-byte runs per row.
+    int wkoff[NLW];
 #pragma unroll
-        for (int j = 0; j < NLW; ++j) {
-            int X, gb;
-            if constexpr (LG == 4) {
-                X = h * NCW + (j >> 1) * 4 + g;
-                gb = j & 1;
-            } else {
-                X = h * NCW + 2 * j + (g >> 1);
-                gb = g & 1;
-            }
-            dst[j] = load_stream16(wrow + min(k_s + gb * kStepK + X * kGranK, H - 16));
+    for (int j = 0; j < NLW; ++j) {
+        int X, gb;
+        if constexpr (LG == 4) {
+            X = h * NCW + (j >> 1) * 4 + g;
+            gb = j & 1;
+        } else {
+            X = h * NCW + 2 * j + (g >> 1);
+            gb = g & 1;
         }
+        wkoff[j] = gb * kStepK + X * kGranK;
+    }
+    auto row_of = [&](int round) {
+        const int tile = (round * nblk + (int)blockIdx.x) * VTW + vt;
+        return min(tile * 16 + i16, V - 1);
+    };
+    auto wload = [&](const uint8_t* wrow, int k_s, uint4(&dst)[NLW]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < NLW; ++j) dst[j] = load_stream16(wrow + min(k_s + wkoff[j], H - 16));
     };
 
     f32x4_t acc[NCW][RT];
-    f32x4_t part[RT];
     // Activation codes of the next two slabs (slot n % 2 holds slab n's).
     uint4 st[2][UPT][2];
     // Weights of PF slabs in flight: slot (it % PF) holds slab it's bytes.
     uint4 wb[PF][NLW];
+    // Weight operands of the chain in hand: instruction t's holds only
+    // dword t; the other dwords stay zero for the whole kernel.
+    uint4 bq[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) bq[t] = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int X = 0; X < NCW; ++X)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) acc[X][rt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) part[rt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     for (int r = threadIdx.x; r < RP; r += NTHREADS) xsc[r] = r < R ? xscale[r] : 0.0f;
+    // Positions (slab index within the hidden dimension, round) of the slab
+    // being computed, of the weights PF - 1 slabs ahead and of the activation
+    // codes two slabs ahead; the last two stop at the last slab.
+    int cs = 0, cround = 0;
+    int ws_ = 0, wround = 0, wit = 0;
+    int ss = 0, sit = 0;
+    auto adv = [&](int& sl, int& rd) {
+        if (++sl == NS) {
+            sl = 0;
+            ++rd;
+        }
+    };
     stage_load(0, st[0]);
     stage_write(0, st[0], xs[0]);
-    stage_load(min(1, total - 1) % NS, st[1]);
+    if (sit + 1 < total) {
+        ++sit;
+        ss = ss + 1 == NS ? 0 : ss + 1;
+    }
+    stage_load(ss * kSlabK, st[1]);
+    const uint8_t* wrow = W + (size_t)row_of(0) * H;
 #pragma unroll
-    for (int p = 0; p + 1 < PF; ++p) wload(min(p, total - 1), wb[p]);
+    for (int p = 0; p + 1 < PF; ++p) {
+        wload(wrow, ws_ * kSlabK, wb[p]);
+        if (wit + 1 < total) {
+            ++wit;
+            adv(ws_, wround);
+            if (ws_ == 0) wrow = W + (size_t)row_of(wround) * H;
+        }
+    }
+    const float* swp = wscale + row_of(0);
     __syncthreads();
 
     // One slab: SL = it % PF (a compile-time slot, the loop is unrolled by PF).
     auto slab = [&](auto sl_tag, int it) __attribute__((always_inline)) {
         constexpr int SL = decltype(sl_tag)::value;
-        static_assert(PF % 2 == 0, "the staging slots follow it % 2");
-        const int s = it % NS;
+        const int s = cs;
         const bool more = it + 1 < total;
-        // Activation codes two slabs ahead (their slot held slab it's codes,
-        // already in LDS), then the weights PF - 1 slabs ahead.
-        // Unconditional (clamped to the last slab): a load inside a branch
-        // would make the compiler wait for every load in flight.
-        stage_load(min(it + 2, total - 1) % NS, st[SL % 2]);
-        wload(min(it + PF - 1, total - 1), wb[(SL + PF - 1) % PF]);
+        uint4* xb = xs[SL & 1];
+        // A operands of this slab, chain by chain: chain XL + 1's are read
+        // while chain XL's MFMAs run (at most two chains' held at once), the
+        // first while the weights are converted.
+        uint4 a[NCW][RT];
+        auto read_a = [&](int XL) __attribute__((always_inline)) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                a[XL][rt] = xb[((h * NCW + XL) * 4 + g) * RP + rt * 16 + i16];
+        };
+        read_a(0);
+        // Activation codes two slabs ahead (their slot held this slab's
+        // codes, already in LDS), then the weights PF - 1 slabs ahead.
+        if (sit + 1 < total) {
+            ++sit;
+            ss = ss + 1 == NS ? 0 : ss + 1;
+        }
+        stage_load(ss * kSlabK, st[SL % 2]);
+        wload(wrow, ws_ * kSlabK, wb[(SL + PF - 1) % PF]);
+        if (wit + 1 < total) {
+            ++wit;
+            adv(ws_, wround);
+            if (ws_ == 0) wrow = W + (size_t)row_of(wround) * H;
+        }
         // This tile's row scale, loaded every slab so that no load sits in
         // the branch that stores (a load there stalls the prefetches above).
-        const float sw = wscale[min(tile_of(it) * 16 + i16, V - 1)];
-        uint4* xb = xs[it & 1];
-        // Chain XL's weight operand bq[t] holds only dword t; o[] are the
-        // BF16 pairs after the transposes.
-        auto chain_mfma = [&](int XL, const uint4(&bq)[4]) __attribute__((always_inline)) {
-            const int X = h * NCW + XL;
-            uint4 a[RT];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) a[rt] = xb[(X * 4 + g) * RP + rt * 16 + i16];
+        const float sw = *swp;
+        // The next slab's activations into the other buffer (read by every
+        // wave in the previous slab, before its barrier); its conversion
+        // overlaps this slab's MFMAs.
+        if (more) stage_write((s + 1 == NS ? 0 : s + 1) * kSlabK, st[(SL + 1) % 2],
+                              xs[(SL + 1) & 1]);
+        auto chain_mfma = [&](int XL, uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3)
+            __attribute__((always_inline)) {
+            if (XL + 1 < NCW) read_a(XL + 1);
+            bq[0].x = p0;
+            bq[1].y = p1;
+            bq[2].z = p2;
+            bq[3].w = p3;
             // Instruction t of every row tile before instruction t + 1:
             // consecutive MFMAs use different accumulators.
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) acc[XL][rt] = mfma_bf16(a[rt], bq[t], acc[XL][rt]);
-            __builtin_amdgcn_sched_barrier(0);
+                for (int rt = 0; rt < RT; ++rt)
+                    acc[XL][rt] = mfma_bf16(a[XL][rt], bq[t], acc[XL][rt]);
         };
         if constexpr (LG == 4) {
 #pragma unroll
@@ -750,11 +814,7 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
                 xpose4(a2[0], a2[1], a2[2], a2[3]);
                 xpose4(a2[4], a2[5], a2[6], a2[7]);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint4 bq[4] = {make_uint4(a1[q], 0, 0, 0), make_uint4(0, a1[4 + q], 0, 0),
-                                         make_uint4(0, 0, a2[q], 0), make_uint4(0, 0, 0, a2[4 + q])};
-                    chain_mfma(4 * j + q, bq);
-                }
+                for (int q = 0; q < 4; ++q) chain_mfma(4 * j + q, a1[q], a1[4 + q], a2[q], a2[4 + q]);
             }
         } else {
 #pragma unroll
@@ -766,16 +826,10 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
                 xpose4(o[0], o[1], o[2], o[3]);
                 xpose4(o[4], o[5], o[6], o[7]);
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const uint4 bq[4] = {make_uint4(o[2 * c], 0, 0, 0),
-                                         make_uint4(0, o[4 + 2 * c], 0, 0),
-                                         make_uint4(0, 0, o[2 * c + 1], 0),
-                                         make_uint4(0, 0, 0, o[5 + 2 * c])};
-                    chain_mfma(2 * j + c, bq);
-                }
+                for (int c = 0; c < 2; ++c)
+                    chain_mfma(2 * j + c, o[2 * c], o[4 + 2 * c], o[2 * c + 1], o[5 + 2 * c]);
             }
         }
-        if (more) stage_write((it + 1) % NS, st[(SL + 1) % 2], xs[(it + 1) & 1]);
         // End of a 4096-k tile (or of the hidden dimension): the tree
         // ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7)) -- each wave its
         // chains' subtree, the workgroup's waves of a tile through LDS in
@@ -820,7 +874,7 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
             if (h == 0) {
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
-                    part[rt] = (s < kSlabsPerTile) ? sub[rt] : part[rt] + sub[rt];
+                    partl[vt][rt][lane] = (s < kSlabsPerTile) ? sub[rt] : partl[vt][rt][lane] + sub[rt];
             }
 #pragma unroll
             for (int X = 0; X < NCW; ++X)
@@ -828,7 +882,7 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
                 for (int rt = 0; rt < RT; ++rt) acc[X][rt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         }
         if (s + 1 == NS && h == 0) {
-            const int tile = tile_of(it);
+            const int tile = (cround * nblk + (int)blockIdx.x) * VTW + vt;
             const int v = tile * 16 + i16;
             if (tile < ntiles && v < V) {
                 // Row offsets computed here, once per vocab tile: an opaque
@@ -838,11 +892,12 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
                 asm volatile("" : "+s"(Vq));
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
+                    const f32x4_t pt = partl[vt][rt][lane];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = rt * 16 + g * 4 + e;
                         if (r < R) {
-                            const float y = (part[rt][e] * xsc[r]) * sw;
+                            const float y = (pt[e] * xsc[r]) * sw;
                             out[(size_t)r * Vq + v] = f32_to_bf16_rne(y);
                         }
                     }
@@ -850,6 +905,8 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
                 }
             }
         }
+        adv(cs, cround);
+        if (cs == 0) swp = wscale + row_of(cround);
         __syncthreads();
     };
 
