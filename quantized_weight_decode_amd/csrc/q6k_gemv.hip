@@ -26,7 +26,8 @@
 // with v_alignbit funnel shifts (super-blocks are only 2-byte aligned; the
 // shift folds the misalignment and the field's bit position). While item it
 // is computed from one buffer, item it + 1 has been written to the other
-// and item it + 2 is in flight in registers. The -32 offset is folded into
+// and items it + 2 .. it + PF are in flight in registers (PF = 2: a deeper
+// ring costs registers and occupancy and measured slower at every row count). The -32 offset is folded into
 // the integer dot: the staging step stores -32 * sum(q8) per sub-block next
 // to the q8 values.
 #include "qhead_device.h"
@@ -82,7 +83,7 @@ __device__ __forceinline__ void q6_stage_tile(Q6Lds<R>& L, const uint8_t* q8, in
     }
 }
 
-template <int R, int T, int WAVES, int MAXB, int BPC>
+template <int R, int T, int WAVES, int MAXB, int BPC, int PF>
 __global__ void __launch_bounds__(WAVES * kWave, (WAVES * BPC + 3) / 4)
 q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ q8, int H, int V,
                 uint16_t* __restrict__ out, int nsuper) {
@@ -204,17 +205,28 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
 
             float acc[NP];
             int bi = 0, s = 0;
-            // Item `it` is in LDS buffer `buf`; item it + 1 is in flight in
-            // `gn` and goes to the other buffer; `gf` is free and receives
-            // item it + 2. `buf` is it's parity (a constant at each call).
-            auto step = [&](int it, int buf, u32x4_t (&gf)[T], const u32x4_t (&gn)[T]) {
-                // (bi, s) of items it + 1 and it + 2, clamped to the last item
-                int bi1 = bi, s1 = s;
-                if (it + 1 < nitems) { if (++s1 == nseg) { s1 = 0; ++bi1; } }
-                int bi2 = bi1, s2 = s1;
-                if (it + 2 < nitems) { if (++s2 == nseg) { s2 = 0; ++bi2; } }
-                issue(bi2, s2, gf);
-                stage(gn, buf ^ 1);
+            // Ring of PF items: slot it % PF holds item it's chunks from its
+            // issue (PF - 1 steps ahead) until step it - 1 writes them to LDS
+            // buffer it & 1; step it then computes item it from that buffer,
+            // with items it + 2 .. it + PF in flight. The issue position
+            // (pbi, ps) stops at the last item.
+            u32x4_t gr[PF][T];
+            int pbi = 0, ps = 0, pit = 0;
+            auto next_issue = [&]() {
+                if (pit + 1 < nitems) {
+                    ++pit;
+                    if (++ps == nseg) {
+                        ps = 0;
+                        ++pbi;
+                    }
+                }
+            };
+            auto step = [&](auto sl_tag, int it) __attribute__((always_inline)) {
+                constexpr int SL = decltype(sl_tag)::value;
+                constexpr int buf = SL & 1;
+                if (it + 1 < nitems) stage(gr[(SL + 1) % PF], buf ^ 1);
+                issue(pbi, ps, gr[SL]);
+                next_issue();
                 if (s == 0) {
 #pragma unroll
                     for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
@@ -288,25 +300,23 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                     ++s;
                 }
             };
-            u32x4_t gA[T], gB[T];
             if (nitems > 0) {
-                issue(0, 0, gA);
-                stage(gA, 0);
-                int bi1 = 0, s1 = 0;
-                if (nitems > 1) { if (++s1 == nseg) { s1 = 0; ++bi1; } }
-                issue(bi1, s1, gB);
+#pragma unroll
+                for (int i = 0; i < PF; ++i) {
+                    issue(pbi, ps, gr[i]);
+                    next_issue();
+                }
+                stage(gr[0], 0);
             }
-            // The loop body always runs both steps: a conditional second
-            // step would let the loop back edge carry loads into gA still in
-            // flight, and the wait counters at the loop head would then
-            // drain every load (including item it + 1's) before issuing.
             int it = 0;
 #pragma unroll 1
-            for (; it + 1 < nitems; it += 2) {
-                step(it, 0, gA, gB);
-                step(it + 1, 1, gB, gA);
-            }
-            if (it < nitems) step(it, 0, gA, gB);
+            for (; it + PF <= nitems; it += PF)
+                static_for<PF>([&](auto sl) __attribute__((always_inline)) {
+                    step(sl, it + decltype(sl)::value);
+                });
+            static_for<PF>([&](auto sl) __attribute__((always_inline)) {
+                if (it + decltype(sl)::value < nitems) step(sl, it + decltype(sl)::value);
+            });
         }
 
 #pragma unroll
@@ -318,7 +328,7 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     }
 }
 
-template <int R, int T, int WAVES, int MAXB, int BPC>
+template <int R, int T, int WAVES, int MAXB, int BPC, int PF>
 static hipError_t launch_q6k(const uint8_t* blocks, const uint8_t* q8, int H, int V,
                              uint16_t* out, const DeviceInfo& dev, hipStream_t stream) {
     const int64_t NB = (V + T - 1) / T;
@@ -327,7 +337,7 @@ static hipError_t launch_q6k(const uint8_t* blocks, const uint8_t* q8, int H, in
     const int64_t TW = nblk * WAVES;
     const int64_t per_wave = (NB + TW - 1) / TW;
     const int nsuper = (int)((per_wave + MAXB - 1) / MAXB);
-    hipLaunchKernelGGL((q6k_gemv_kernel<R, T, WAVES, MAXB, BPC>), dim3((unsigned)nblk),
+    hipLaunchKernelGGL((q6k_gemv_kernel<R, T, WAVES, MAXB, BPC, PF>), dim3((unsigned)nblk),
                        dim3(WAVES * kWave), 0, stream, blocks, q8, H, V, out, nsuper);
     return hipGetLastError();
 }
@@ -337,7 +347,7 @@ hipError_t run_q6k(const uint8_t* blocks, const uint8_t* q8, int R, int H, int V
     switch (R) {
 #define QH_Q6_CASE(RR, TT, WV, MB, BPC) \
     case RR:                            \
-        return launch_q6k<RR, TT, WV, MB, BPC>(blocks, q8, H, V, out, dev, stream);
+        return launch_q6k<RR, TT, WV, MB, BPC, 2>(blocks, q8, H, V, out, dev, stream);
         QH_Q6_CASE(1, 4, 8, 12, 2)
         QH_Q6_CASE(2, 2, 12, 8, 2)
         QH_Q6_CASE(3, 2, 16, 12, 1)

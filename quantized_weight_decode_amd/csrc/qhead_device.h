@@ -8,7 +8,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace qh {
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), unrolled:
+// loop bodies with compile-time slot indices (register rings of loads).
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 

@@ -27,9 +27,6 @@
 // Eight chains keep the VALU kernel's weight reads in 128-byte runs per row
 // (8 lanes x 16 bytes), which stream near the rate of longer runs, while the
 // MFMA kernel holds 8 chains x 8 row tiles of accumulators at 128 rows.
-#include <type_traits>
-#include <utility>
-
 #include "qhead_device.h"
 #include "qhead_internal.h"
 
@@ -67,16 +64,6 @@ __device__ __forceinline__ void xpose4(uint32_t& r0, uint32_t& r1, uint32_t& r2,
     auto e = __builtin_amdgcn_permlane16_swap(r2, r3, false, false);
     r2 = e[0];
     r3 = e[1];
-}
-
-// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), unrolled.
-template <int N, typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
 }
 
 // 16 E4M3 bytes -> 8 BF16 pairs (pair p = bytes 2p, 2p+1), exact.
