@@ -617,21 +617,26 @@ ORC_API double orc_e8m0(uint8_t e) {
     return ldexp(1.0, (int)e - 127);
 }
 
-/* E2M1 with E8M0 per-group scales and no global -> BF16, over a flat tensor
- * of `total` values in `groups` groups of total/groups consecutive values
- * ("fp8_lut.rs", dequant_nvfp4_e8m0_to_bf16): out = bf16(fl32(e2m1 * scale)). */
+/* E2M1 with E8M0 group scales and no global -> BF16 ("fp8_lut.rs",
+ * dequant_nvfp4_e8m0_to_bf16, and its E8M0 table). The tensor is `total`
+ * values; value j is nibble j of `packed` (the low half of byte j/2 for even
+ * j, the high half for odd j), and belongs to group j / (total/groups), whose
+ * scale byte is scales[group]. Its BF16 is the nearest-even rounding of the
+ * binary32 value of e2m1 * 2^(e-127) (exact in binary32 unless it overflows
+ * to infinity). Each packed byte is decoded once, both of its values. */
 ORC_API void orc_dequant_fp4_e8m0_bf16(const uint8_t* packed, const uint8_t* scales,
                                        int64_t total, int64_t groups, uint16_t* out) {
-    int64_t block = total / groups;
+    const int64_t per_group = total / groups;
+    const int64_t nbytes = (total + 1) / 2;
 #pragma omp parallel for schedule(static)
-    for (int64_t gi = 0; gi < groups; gi++) {
-        double sc = orc_e8m0(scales[gi]);
-        for (int64_t e = 0; e < block; e++) {
-            int64_t flat = gi * block + e;
-            uint8_t byte = packed[flat / 2];
-            uint8_t nib = (flat % 2 == 0) ? (byte & 15) : (byte >> 4);
-            float y = (float)(orc_e2m1(nib) * sc); /* exact unless it leaves binary32's range */
-            out[flat] = orc_bf16_rne((double)y);
+    for (int64_t b = 0; b < nbytes; b++) {
+        const uint8_t two = packed[b];
+        const uint8_t nib[2] = {(uint8_t)(two & 15), (uint8_t)(two >> 4)};
+        for (int half = 0; half < 2; half++) {
+            const int64_t j = 2 * b + half;
+            if (j >= total) break;
+            const double value = orc_e2m1(nib[half]) * orc_e8m0(scales[j / per_group]);
+            out[j] = orc_bf16_rne((double)(float)value);
         }
     }
 }
