@@ -96,11 +96,6 @@ fp8_gemv_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
             const int k0 = tt * kTileK;
             const int klen = min(kTileK, H - k0);
             const int nseg = (klen + kSegK - 1) / kSegK;
-            if (NT > 1 || sj == 0) {
-                __syncthreads();
-                stage_tile<R, WAVES * kWave>(xs, xin, H, k0, nseg);
-                __syncthreads();
-            }
             // This wave's bands in this super-iteration, walked as one flat
             // list of (band, segment) items so that the next item's weights
             // are always in flight while the current one is computed.
@@ -239,7 +234,18 @@ fp8_gemv_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
                 }
             };
             uint4 bufA[T], bufB[T];
-            if (nitems > 0) load_item(0, 0, bufA);
+            // Up to 4 rows (HBM-bound launches) the first item's loads go out
+            // before the activation tile is staged, so their latency and the
+            // staging's overlap; with more rows the registers they would hold
+            // through the staging are scarcer than the latency.
+            constexpr bool kEarly = R <= 4;
+            if (kEarly && nitems > 0) load_item(0, 0, bufA);
+            if (NT > 1 || sj == 0) {
+                __syncthreads();
+                stage_tile<R, WAVES * kWave>(xs, xin, H, k0, nseg);
+                __syncthreads();
+            }
+            if (!kEarly && nitems > 0) load_item(0, 0, bufA);
             int it = 0;
 #pragma unroll 1
             for (; it + 1 < nitems; it += 2) {
@@ -303,6 +309,13 @@ hipError_t run_fp8_w8a16(const uint8_t* W, const float* wscale, const uint16_t* 
     // Heads with few vocab rows (the SiLU down projection's 7168): with
     // 4-row bands the 9..16-row shape gives a wave fewer than two bands and
     // leaves waves idle; 2-row bands in 16-wave groups keep them busy.
+    // Heads of fewer than 4 two-row bands per wave of a 32-wave-per-CU grid
+    // (the 32000 x 4096 head): 1 and 2 rows take the shapes that measured
+    // fastest there (32000 x 4096 with 7 rotated copies: 1 row 27.7 ->
+    // 24.6 us, 2 rows 29.4 -> 25.5 us; on the 155136-row head they lose 3 %).
+    const bool narrow = (int64_t)(V + 1) / 2 < (int64_t)dev.num_cus * 32 * 4;
+    if (narrow && R == 1) return launch_fp8<1, 2, 4, 12, 8>(W, wscale, x, H, V, out, dev, stream);
+    if (narrow && R == 2) return launch_fp8<2, 4, 16, 12, 1>(W, wscale, x, H, V, out, dev, stream);
     const bool skinny = R >= 9 && (int64_t)(V + 3) / 4 < 2 * (int64_t)dev.num_cus * 8;
     if (skinny) {
         switch (R) {
