@@ -52,3 +52,37 @@ def test_workload_table():
     cfg = synth.CONFIGS[fp8.cfg]
     assert (cfg.vocab, cfg.hidden) == (155136, 8192)
     assert [int(r) for r in fp8.rows.split(",")] == [1, 2, 4, 8, 16]
+
+
+def test_compute_roofs():
+    """The per-call compute roofs bench.py reports next to the HBM roof: the
+    VALU issue time of (R + 2)/2 lane-slots per FP8 weight byte at 64
+    lane-operations per CU per cycle, and for W8A8 at 16+ rows the matrix-unit
+    time of 32 * ceil(R/16) 16-cycle MFMAs per 16 vocab rows and 256 k."""
+    V, H = 155136, 8192
+    rate = 256 * 64 * 2.4e9
+    us, unit = bench.compute_roof_us("fp8", V, H, 16)
+    assert unit == "valu" and abs(us - V * H / 2 * 18 / rate * 1e6) < 1e-6
+    us64, _ = bench.compute_roof_us("fp8_rows64", V, H, 64)
+    assert abs(us64 - 4 * us) < 1e-6  # four 16-row passes
+    V, H = 129280, 7168
+    us, unit = bench.compute_roof_us("w8a8", V, H, 128)
+    mfma = (V // 16) * (H // 256) * 32 * 8 * 16 / (1024 * 2.4e9) * 1e6
+    assert unit == "mfma" and abs(us - mfma) < 1e-6
+    us1, unit1 = bench.compute_roof_us("w8a8", V, H, 1)
+    assert unit1 == "valu" and abs(us1 - V * H / 2 * 3 / rate * 1e6) < 1e-6
+    # 300 rows = 128 + 128 + 44: three passes, the last of 3 row tiles
+    us300, _ = bench.compute_roof_us("w8a8", V, H, 300)
+    assert abs(us300 - mfma * (8 + 8 + 3) / 8) < 1e-6
+    assert bench.compute_roof_us("dequant", V, H, 0) is None
+
+
+def test_weight_copies_exceed_the_cache():
+    for name in bench.E4M3_HEADS:
+        cfg = synth.CONFIGS[bench.WORKLOADS[name].cfg]
+        n = bench.weight_copies(name, cfg.vocab, cfg.hidden)
+        wbytes = bench.algorithmic_bytes(name, cfg.vocab, cfg.hidden, 0)
+        assert n == 1 or n * wbytes >= bench.ROTATE_BYTES, name
+        assert n * wbytes >= min(bench.ROTATE_BYTES, wbytes)
+    cfg = synth.CONFIGS[synth.FP8_32000X4096]
+    assert bench.weight_copies("fp8_32000", cfg.vocab, cfg.hidden) >= 3
