@@ -586,7 +586,7 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
     constexpr int NTHREADS = WAVES * kWave;
     constexpr int NCW = kChains / CS;            // chains per wave
     constexpr int LG = NCW >= 4 ? 4 : 2;         // chains per weight-load group
-    constexpr int NLW = 2 * NCW / LG;            // 16-byte weight loads per slab
+    constexpr int NLW = NCW / 2;                 // 16-byte weight loads per slab
     constexpr int SLAB_VEC = kChains * 4 * RP;   // uint4 per staged slab
     constexpr int UNITS = kChains * RP;          // (chain, row) staging units per slab
     constexpr int UPT = (UNITS + NTHREADS - 1) / NTHREADS;
@@ -611,8 +611,14 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
     const int nblk = gridDim.x;
 
     // Staging: this thread's units u = threadIdx.x + j * NTHREADS = (chain X,
-    // row r), rows fastest (consecutive threads write consecutive 16-byte LDS
-    // words). Rows >= R load row R - 1 and are staged as they come: an MFMA
+    // row r), chains fastest, so that 8 consecutive lanes load one 128-byte
+    // run of a row (a lane per row would touch a cache line per lane). In LDS
+    // the row slots of chain X are rotated by X within each 16-row block:
+    // row r of chain X sits at slot (r & ~15) | ((r + X) & 15). A 16-byte LDS
+    // access is served 8 lanes at a time over 32 banks (128 bytes); the 8
+    // lanes of a write (8 chains, one row) then take 8 distinct 16-byte bank
+    // groups, and so do 8 consecutive rows of a tile that an operand read
+    // takes. Rows >= R load row R - 1 and are staged as they come: an MFMA
     // row of A only feeds the same row of the result, and those rows are
     // never stored. Columns k >= H are staged as zero.
     const uint8_t* ssrc[UPT];
@@ -623,10 +629,10 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
         const int u = (int)threadIdx.x + j * NTHREADS;
         sact[j] = UNITS % NTHREADS == 0 || u < UNITS;
         const int uu = min(u, UNITS - 1);
-        const int r = uu % RP;
-        const int X = uu / RP;
+        const int X = uu % kChains;
+        const int r = uu / kChains;
         ssrc[j] = xq + (size_t)min(r, R - 1) * H;
-        sldo[j] = X * 4 * RP + r;
+        sldo[j] = X * 4 * RP + ((r & ~15) | ((r + X) & 15));
         skx[j] = X * kGranK;
     }
     // Loads stay unconditional (clamped addresses): a load inside a branch
@@ -747,9 +753,10 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
         // first while the weights are converted.
         uint4 a[NCW][RT];
         auto read_a = [&](int XL) __attribute__((always_inline)) {
+            const int X = h * NCW + XL;
+            const int base = (X * 4 + g) * RP + ((i16 + X) & 15);
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                a[XL][rt] = xb[((h * NCW + XL) * 4 + g) * RP + rt * 16 + i16];
+            for (int rt = 0; rt < RT; ++rt) a[XL][rt] = xb[base + rt * 16];
         };
         read_a(0);
         // Activation codes two slabs ahead (their slot held this slab's
