@@ -40,13 +40,18 @@ constexpr int kQSbPerTile = kQTileK / 256;
 
 // LDS per workgroup, sized by the row count so that small R leaves room for
 // several workgroups per CU.
-// The q8 values of a super-block (256 k) take 256 + 16 bytes and its 16
-// sub-block offsets 16 + 1 words: the super-blocks one half wave reads at
-// once then start in different LDS banks.
+// The q8 values of a super-block (256 k) take 256 + 16 bytes. Its 16
+// sub-block offsets take 16 words, in slot sb ^ ((sb >> 1) & 1) for super-
+// block sb: a 4-byte LDS read serves 32 lanes at a time over 32 banks, and
+// the two half waves in it read super-blocks 4s + i and 4s + i + 2 (i = 0,
+// 1), whose offsets then sit in the two different 16-bank halves.
 constexpr int kQPadSb = 256 + 16;
-constexpr int kOffPadSb = 16 + 1;
+constexpr int kOffPadSb = 16;
 __device__ __forceinline__ int q_pos(int k) { return (k >> 8) * kQPadSb + (k & 255); }
-__device__ __forceinline__ int off_pos(int k) { return (k >> 8) * kOffPadSb + ((k & 255) >> 4); }
+__device__ __forceinline__ int off_pos(int k) {
+    const int sb = k >> 8;
+    return (sb ^ ((sb >> 1) & 1)) * kOffPadSb + ((k & 255) >> 4);
+}
 
 template <int R>
 struct alignas(16) Q6Lds {
@@ -69,15 +74,20 @@ __device__ __forceinline__ void q6_stage_tile(Q6Lds<R>& L, const uint8_t* q8, in
         const uint32_t head = src[0];
         const _Float16 d16 = __builtin_bit_cast(_Float16, (uint16_t)(head & 0xFFFFu));
         L.d8[r][j] = (float)d16;
+        // the block's 32 values as two 16-byte LDS writes (a 4-byte write
+        // per value word would put 8 lanes on each bank)
+        uint32_t w[8];
         int s0 = 0, s1 = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const uint32_t w = src[1 + i];
-            *reinterpret_cast<uint32_t*>(&L.q[r][q_pos(j * 32 + 4 * i)]) = w;
-            const int sum4 = __builtin_amdgcn_sdot4((int)w, 0x01010101, 0, false);
+            w[i] = src[1 + i];
+            const int sum4 = __builtin_amdgcn_sdot4((int)w[i], 0x01010101, 0, false);
             if (i < 4) s0 += sum4;
             else s1 += sum4;
         }
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(&L.q[r][q_pos(j * 32)]);
+        dst[0] = u32x4_t{w[0], w[1], w[2], w[3]};
+        dst[1] = u32x4_t{w[4], w[5], w[6], w[7]};
         L.off[r][off_pos(j * 32)] = -32 * s0;
         L.off[r][off_pos(j * 32 + 16)] = -32 * s1;
     }
@@ -93,6 +103,7 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     constexpr int kItemBytes = 4 * kQ6KBlockBytes;  // 840
     static_assert(NP <= 64 && R <= 8, "T*R must be <= 64, R <= 8");
     static_assert(kItemBytes + 15 <= 64 * 16, "an item must fit one 16-byte load per lane");
+    static_assert((kItemBytes + 13) / 16 + 2 <= 61, "the shifted chunks stay in the row's buffer");
     __shared__ Q6Lds<R> L;
     // wave-private weight staging, two buffers: [wave][item parity][row t]
     // [1024 bytes]. Item it + 1 is written into one buffer at the start of
@@ -109,10 +120,13 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     const int nsb = H / 256;
     const size_t rowbytes = (size_t)nsb * kQ6KBlockBytes;
 
-    // lane -> (super-block within the item, sub-block t = 8n + 2c + h). Half
-    // waves take super-blocks {0, 2} and {1, 3}: those two start 105 dwords
-    // apart, so their fields fall in different LDS bank groups (0 and 1,
-    // 52.5 dwords apart, would share them).
+    // lane -> (super-block within the item, sub-block t = 8n + 2c + h). A
+    // 4-byte LDS read serves 32 lanes at a time over 32 banks; its two half
+    // waves take super-blocks {0, 2} or {1, 3}. Super-blocks 2 and 3 are
+    // staged 32 bytes later than their place in the item (see `stage`):
+    // 137 dwords from super-block 0, 105 + 8 from 1, which puts the ql and
+    // qh windows of the two half waves in disjoint banks at every item
+    // misalignment (105 dwords alone leaves two qh banks shared).
     const int sbi = (((lane >> 4) & 1) << 1) | (lane >> 5);
     const int t16 = lane & 15;
     const int n = t16 >> 3, c = (t16 >> 1) & 3, h = t16 & 1;
@@ -128,7 +142,7 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     // The offsets count from the block's first staging buffer and include
     // this wave's buffers (a multiple of 4 bytes).
     const int qh_back = hi_shift < 4 ? 1 : 0;
-    const int p_sb = wave * (2 * T * kWave * 16) + sbi * kQ6KBlockBytes;
+    const int p_sb = wave * (2 * T * kWave * 16) + sbi * kQ6KBlockBytes + (sbi >= 2 ? 32 : 0);
     const int p_ql = p_sb + ql_off;
     const int p_qh = p_sb + qh_off - qh_back;
     const int b_qh = 8 * qh_back + hi_shift - 4;
@@ -198,9 +212,19 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                     g[t] = *reinterpret_cast<const u32x4_t*>(p16 + 16 * ch);
                 }
             };
+            // Chunk j goes to slot j, from chunk 26 on to slot j + 2: super-
+            // blocks 2 and 3 (item bytes >= 420 + 0..14) land 32 bytes
+            // later. Chunks 26 and 27 also keep slot j for the tail of
+            // super-block 1 (bytes < 434). The last chunk an item needs is
+            // 53 (slot 55); lanes 62 and 63 hold copies of it and write
+            // nothing.
+            const int sslot = lane < 26 ? lane : lane + 2;
             auto stage = [&](const u32x4_t (&g)[T], int buf) {
 #pragma unroll
-                for (int t = 0; t < T; ++t) WB[wave][buf][t][lane] = g[t];
+                for (int t = 0; t < T; ++t) {
+                    if (lane < 62) WB[wave][buf][t][sslot] = g[t];
+                    if (lane == 26 || lane == 27) WB[wave][buf][t][lane] = g[t];
+                }
             };
 
             float acc[NP];
