@@ -566,17 +566,26 @@ hipError_t launch_valu_split(const uint8_t* W, const float* ws, const uint8_t* x
 // k_s + 16c and B at k_s + 128 + 16c. The activations of a slab are staged
 // in LDS by the whole workgroup as the dense A operands, [chain][lane group
 // g][row] x 16 bytes holding the BF16 pairs (A pair g, A pair 4+g, B pair g,
-// B pair 4+g) -- the pairs that step g of instructions 0..3 multiply. The
-// weights of four chains come from two 16-byte loads per lane (lane group
+// B pair 4+g) -- the pairs that step g of instructions 0..3 multiply. A
+// lane takes the weights of four chains as two 16-byte pieces (lane group
 // g: chain g of the group, granule A, then B), or, with two chains per
-// wave, those of a chain pair from one load (lane group g: chain g/2,
+// wave, those of a chain pair as one piece (lane group g: chain g/2,
 // granule g & 1); they are converted to BF16 pairs and transposed across
 // lane groups so that dword q of lane group g holds the pair that
 // instruction q's step g multiplies; instruction t then uses a weight
-// operand holding only dword t, so its step g adds exactly that one pair. At the end of each 4096-k tile the chains go
+// operand holding only dword t, so its step g adds exactly that one pair.
+// The pieces come straight from HBM (LW = 0: 16-byte loads at a row stride)
+// or, with LW = 1, through LDS: the workgroup reads each slab's weights in
+// 256-byte runs per row (piece p = chain + 8 * granule of row w per
+// thread), PF - 1 slabs ahead, and stages them raw one slab ahead, piece p
+// of workgroup row w at slot 16w + (p ^ (w & 7)) (8 lanes of a 16-byte
+// access take 8 distinct bank groups when a row is written and when 8 rows'
+// pieces are read). LW = 1 pays with one wave per tile (4 pieces per lane
+// and slab, loads far apart otherwise); with more waves per tile the direct
+// loads measured faster. At the end of each 4096-k tile the chains go
 // through the tree (across the waves of a tile through LDS) and restart
 // from zero.
-template <int RT, int VTW, int CS, int PF>
+template <int RT, int VTW, int CS, int PF, int LW>
 __global__ void __launch_bounds__(VTW * CS * kWave, (VTW * CS + 3) / 4)
 w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
                  const uint8_t* __restrict__ xq, const float* __restrict__ xscale, int R, int H,
@@ -586,7 +595,9 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
     constexpr int NTHREADS = WAVES * kWave;
     constexpr int NCW = kChains / CS;            // chains per wave
     constexpr int LG = NCW >= 4 ? 4 : 2;         // chains per weight-load group
-    constexpr int NLW = NCW / 2;                 // 16-byte weight loads per slab
+    constexpr int NLW = NCW / 2;                 // 16-byte weight pieces per lane per slab
+    constexpr int WRS = NTHREADS / 16;           // LW: workgroup rows one staging pass covers
+    static_assert(WRS % 8 == 0, "at least two waves per workgroup");
     constexpr int SLAB_VEC = kChains * 4 * RP;   // uint4 per staged slab
     constexpr int UNITS = kChains * RP;          // (chain, row) staging units per slab
     constexpr int UPT = (UNITS + NTHREADS - 1) / NTHREADS;
@@ -595,6 +606,7 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
     // the tree's exchange reuses a slab buffer: (CS - 1) partial sums per tile
     static_assert((CS - 1) * VTW * RT * kWave <= SLAB_VEC, "exchange fits a slab buffer");
     __shared__ uint4 xs[2][SLAB_VEC];
+    __shared__ uint4 wl[LW ? 2 : 1][LW ? VTW * 16 * 16 : 1];
     __shared__ float xsc[RP];
     // the tile sums so far of each vocab tile (kept by its wave h = 0)
     __shared__ f32x4_t partl[VTW][RT][kWave];
@@ -693,6 +705,31 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
 #pragma unroll
         for (int j = 0; j < NLW; ++j) dst[j] = load_stream16(wrow + min(k_s + wkoff[j], H - 16));
     };
+    // LW = 1: thread t stages piece t % 16 of workgroup rows t / 16 + j * WRS
+    // (j < NLW; NLW * WRS = VTW * 16 rows), workgroup row w being row w % 16
+    // of the workgroup's tile w / 16; WRS is a multiple of 8, so every j has
+    // the same slot offset. The lane's own pieces sit at wrd[j].
+    const int wr0 = (int)threadIdx.x >> 4;
+    const int wpc = (int)threadIdx.x & 15;
+    const int wslot = 16 * wr0 + (wpc ^ (wr0 & 7));
+    int wrd[NLW];
+#pragma unroll
+    for (int j = 0; j < NLW; ++j) {
+        const int w = vt * 16 + i16;
+        wrd[j] = 16 * w + ((wkoff[j] / kGranK) ^ (w & 7));
+    }
+    auto wrow0_of = [&](int round) { return (round * nblk + (int)blockIdx.x) * VTW * 16 + wr0; };
+    int wrow0 = wrow0_of(0);
+    auto wload_rows = [&](int k_s, uint4(&dst)[NLW]) __attribute__((always_inline)) {
+        const int ko = min(k_s + wpc * kGranK, H - 16);
+#pragma unroll
+        for (int j = 0; j < NLW; ++j)
+            dst[j] = load_stream16(W + (size_t)min(wrow0 + j * WRS, V - 1) * H + ko);
+    };
+    auto wstage = [&](const uint4(&src)[NLW], uint4* dst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < NLW; ++j) dst[wslot + j * NTHREADS] = src[j];
+    };
 
     f32x4_t acc[NCW][RT];
     // Activation codes of the next two slabs (slot n % 2 holds slab n's).
@@ -730,15 +767,27 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
     }
     stage_load(ss * kSlabK, st[1]);
     const uint8_t* wrow = W + (size_t)row_of(0) * H;
-#pragma unroll
-    for (int p = 0; p + 1 < PF; ++p) {
-        wload(wrow, ws_ * kSlabK, wb[p]);
+    // The weights PF - 1 slabs ahead: position advance and load.
+    auto wnext = [&]() {
         if (wit + 1 < total) {
             ++wit;
             adv(ws_, wround);
-            if (ws_ == 0) wrow = W + (size_t)row_of(wround) * H;
+            if (ws_ == 0) {
+                if constexpr (LW) wrow0 = wrow0_of(wround);
+                else wrow = W + (size_t)row_of(wround) * H;
+            }
         }
+    };
+    auto wissue = [&](uint4(&dst)[NLW]) __attribute__((always_inline)) {
+        if constexpr (LW) wload_rows(ws_ * kSlabK, dst);
+        else wload(wrow, ws_ * kSlabK, dst);
+    };
+#pragma unroll
+    for (int p = 0; p + 1 < PF; ++p) {
+        wissue(wb[p]);
+        wnext();
     }
+    if constexpr (LW) wstage(wb[0], wl[0]);
     const float* swp = wscale + row_of(0);
     __syncthreads();
 
@@ -766,11 +815,15 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
             ss = ss + 1 == NS ? 0 : ss + 1;
         }
         stage_load(ss * kSlabK, st[SL % 2]);
-        wload(wrow, ws_ * kSlabK, wb[(SL + PF - 1) % PF]);
-        if (wit + 1 < total) {
-            ++wit;
-            adv(ws_, wround);
-            if (ws_ == 0) wrow = W + (size_t)row_of(wround) * H;
+        wissue(wb[(SL + PF - 1) % PF]);
+        wnext();
+        // This slab's weight pieces: from LDS (staged in the previous slab)
+        // or the load ring.
+        uint4 wv[NLW];
+#pragma unroll
+        for (int j = 0; j < NLW; ++j) {
+            if constexpr (LW) wv[j] = wl[SL & 1][wrd[j]];
+            else wv[j] = wb[SL][j];
         }
         // This tile's row scale, loaded every slab so that no load sits in
         // the branch that stores (a load there stalls the prefetches above).
@@ -778,8 +831,10 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
         // The next slab's activations into the other buffer (read by every
         // wave in the previous slab, before its barrier); its conversion
         // overlaps this slab's MFMAs.
-        if (more) stage_write((s + 1 == NS ? 0 : s + 1) * kSlabK, st[(SL + 1) % 2],
-                              xs[(SL + 1) & 1]);
+        if (more) {
+            stage_write((s + 1 == NS ? 0 : s + 1) * kSlabK, st[(SL + 1) % 2], xs[(SL + 1) & 1]);
+            if constexpr (LW) wstage(wb[(SL + 1) % PF], wl[(SL + 1) & 1]);
+        }
         auto chain_mfma = [&](int XL, uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3)
             __attribute__((always_inline)) {
             if (XL + 1 < NCW) read_a(XL + 1);
@@ -801,8 +856,8 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
                 // Four chains: a1[Q] = pair g of granule A of chain Q's row,
                 // a1[4+Q] its pair 4+g; a2[] the same for granule B.
                 uint32_t a1[8], a2[8];
-                e4m3x16_to_bf16(wb[SL][2 * j], a1);
-                e4m3x16_to_bf16(wb[SL][2 * j + 1], a2);
+                e4m3x16_to_bf16(wv[2 * j], a1);
+                e4m3x16_to_bf16(wv[2 * j + 1], a2);
                 xpose4(a1[0], a1[1], a1[2], a1[3]);
                 xpose4(a1[4], a1[5], a1[6], a1[7]);
                 xpose4(a2[0], a2[1], a2[2], a2[3]);
@@ -816,7 +871,7 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
                 // Chains 2j, 2j+1: o[Q] holds pair g of granule Q's row
                 // (Q = 2c + granule), o[4 + Q] its pair 4 + g.
                 uint32_t o[8];
-                e4m3x16_to_bf16(wb[SL][j], o);
+                e4m3x16_to_bf16(wv[j], o);
                 xpose4(o[0], o[1], o[2], o[3]);
                 xpose4(o[4], o[5], o[6], o[7]);
 #pragma unroll
@@ -915,7 +970,7 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
     });
 }
 
-template <int RT, int VTW, int CS, int PF>
+template <int RT, int VTW, int CS, int PF, int LW = 0>
 hipError_t launch_mfma(const uint8_t* W, const float* ws, const uint8_t* xq, const float* xs,
                        int R, int H, int V, uint16_t* out, const DeviceInfo& dev,
                        hipStream_t stream) {
@@ -923,7 +978,7 @@ hipError_t launch_mfma(const uint8_t* W, const float* ws, const uint8_t* xq, con
     int64_t blocks = (ntiles + VTW - 1) / VTW;
     if (blocks > (int64_t)dev.num_cus) blocks = (int64_t)dev.num_cus;
     const int nrounds = (int)((ntiles + blocks * VTW - 1) / (blocks * VTW));
-    hipLaunchKernelGGL((w8a8_mfma_kernel<RT, VTW, CS, PF>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((w8a8_mfma_kernel<RT, VTW, CS, PF, LW>), dim3((unsigned)blocks),
                        dim3(VTW * CS * kWave), 0, stream, W, ws, xq, xs, R, H, V, out, nrounds);
     return hipGetLastError();
 }
@@ -999,7 +1054,7 @@ hipError_t run_w8a8_gemv(const uint8_t* W, const float* sw, const uint8_t* xq, c
     if (ntiles < (int64_t)dev.num_cus * 4) {
         switch ((R + 15) / 16) {
             case 1:
-                return launch_mfma<1, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
+                return launch_mfma<1, 2, 4, 4, 1>(W, sw, xq, sa, R, H, V, out, dev, stream);
             case 2:
                 return launch_mfma<2, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
             case 3:
@@ -1012,9 +1067,9 @@ hipError_t run_w8a8_gemv(const uint8_t* W, const float* sw, const uint8_t* xq, c
     }
     switch ((R + 15) / 16) {
         case 1:
-            return launch_mfma<1, 8, 1, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma<1, 8, 1, 4, 1>(W, sw, xq, sa, R, H, V, out, dev, stream);
         case 2:
-            return launch_mfma<2, 8, 1, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma<2, 8, 1, 4, 1>(W, sw, xq, sa, R, H, V, out, dev, stream);
         case 3:
             return launch_mfma<3, 4, 2, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
         case 4:
