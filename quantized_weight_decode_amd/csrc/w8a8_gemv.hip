@@ -41,31 +41,6 @@ constexpr int kW8TileK = 4096;                   // k per reduction tile
 constexpr int kSlabsPerTile = kW8TileK / kSlabK;  // 16
 constexpr int kTileVec = kW8TileK / 8;           // uint4 of BF16 per row per tile
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-// Transpose of four dwords across the four 16-lane groups: afterwards
-// register q of lane group g holds what register g of lane group q held.
-__device__ __forceinline__ void xpose4(uint32_t& r0, uint32_t& r1, uint32_t& r2, uint32_t& r3) {
-    auto a = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
-    r0 = a[0];
-    r2 = a[1];
-    auto b = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
-    r1 = b[0];
-    r3 = b[1];
-    auto d = __builtin_amdgcn_permlane16_swap(r0, r1, false, false);
-    r0 = d[0];
-    r1 = d[1];
-    auto e = __builtin_amdgcn_permlane16_swap(r2, r3, false, false);
-    r2 = e[0];
-    r3 = e[1];
-}
-
 // 16 E4M3 bytes -> 8 BF16 pairs (pair p = bytes 2p, 2p+1), exact.
 __device__ __forceinline__ void e4m3x16_to_bf16(const uint4& w, uint32_t (&p)[8]) {
     e4m3x4_to_bf16(w.x, p[0], p[1]);
