@@ -40,12 +40,16 @@ constexpr int kQSbPerTile = kQTileK / 256;
 
 // LDS per workgroup, sized by the row count so that small R leaves room for
 // several workgroups per CU.
-// The q8 values of a super-block (256 k) take 256 + 16 bytes. Its 16
-// sub-block offsets take 16 words, in slot sb ^ ((sb >> 1) & 1) for super-
-// block sb: a 4-byte LDS read serves 32 lanes at a time over 32 banks, and
-// the two half waves in it read super-blocks 4s + i and 4s + i + 2 (i = 0,
-// 1), whose offsets then sit in the two different 16-bank halves.
-constexpr int kQPadSb = 256 + 16;
+// The q8 values of a super-block (256 k) take 256 bytes, unpadded: each
+// 16-lane group of a 16-byte read takes one super-block's 256 contiguous
+// bytes, and padding super-blocks by 16..64 bytes measured 7 times the bank
+// conflict cycles of no padding (raw SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
+// 0.139 against 0.019 at 4 and 8 rows). Its 16 sub-block offsets take 16
+// words, in slot sb ^ ((sb >> 1) & 1) for super-block sb: a 4-byte LDS read
+// serves 32 lanes at a time over 32 banks, and the two half waves in it read
+// super-blocks 4s + i and 4s + i + 2 (i = 0, 1), whose offsets then sit in
+// the two different 16-bank halves.
+constexpr int kQPadSb = 256;
 constexpr int kOffPadSb = 16;
 __device__ __forceinline__ int q_pos(int k) { return (k >> 8) * kQPadSb + (k & 255); }
 __device__ __forceinline__ int off_pos(int k) {
@@ -55,7 +59,7 @@ __device__ __forceinline__ int off_pos(int k) {
 
 template <int R>
 struct alignas(16) Q6Lds {
-    int8_t q[R][kQSbPerTile * kQPadSb];     // q8 values [row][k], padded per super-block
+    int8_t q[R][kQSbPerTile * kQPadSb];     // q8 values [row][k]
     float d8[R][kQTileK / 32];              // fp16 d of each q8 block, as f32
     int32_t off[R][kQSbPerTile * kOffPadSb];  // -32 * sum of q8 per 16-value sub-block, padded
 };
