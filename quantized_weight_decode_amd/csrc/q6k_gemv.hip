@@ -18,22 +18,63 @@
 // sub-block t = the 16 consecutive weights 16t .. 16t+15, whose low bits are
 // 16 consecutive ql bytes and whose high bits are 16 consecutive qh bytes. A
 // wave covers four super-blocks (1024 weights, 840 bytes) of each of its T
-// vocab rows per item. Those 840 bytes are fetched with one fully coalesced
-// 16-byte load per lane (the aligned 16-byte chunks that hold them; a chunk
-// holding at least one byte of the item never crosses a page) and written
-// to one of two wave-private LDS buffers; each lane then reads its fields
-// from LDS as aligned dwords and cuts four 6-bit codes at a time out of them
-// with v_alignbit funnel shifts (super-blocks are only 2-byte aligned; the
-// shift folds the misalignment and the field's bit position). While item it
-// is computed from one buffer, item it + 1 has been written to the other
-// and items it + 2 .. it + PF are in flight in registers (PF = 2: a deeper
-// ring costs registers and occupancy and measured slower at every row count). The -32 offset is folded into
-// the integer dot: the staging step stores -32 * sum(q8) per sub-block next
-// to the q8 values.
+// vocab rows per item. Those 840 bytes are the aligned 16-byte chunks that
+// hold them (a chunk holding at least one byte of the item never crosses a
+// page), loaded straight into one of two wave-private LDS buffers by one
+// fully coalesced global_load_lds_dwordx4 per row (lane l's chunk to slot
+// l); each lane then reads its fields from LDS as aligned dwords and cuts
+// four 6-bit codes at a time out of them with v_alignbit funnel shifts
+// (super-blocks are only 2-byte aligned; the shift folds the misalignment
+// and the field's bit position). While item it is computed from one buffer,
+// item it + 1 is in flight into the other; the wait before each item is
+// placed by hand (lds_dma16), so that the next item's loads stay in flight
+// across the computation. With no register ring, the weights cost no
+// registers between issue and use. The -32 offset is folded into the
+// integer dot: the staging step stores -32 * sum(q8) per sub-block next to
+// the q8 values.
 #include "qhead_device.h"
 #include "qhead_internal.h"
 
 namespace qh {
+
+// Byte offset of an LDS object within the workgroup's LDS allocation: the
+// value M0 takes for a load straight into LDS.
+__device__ __forceinline__ uint32_t lds_byte_offset(const void* p) {
+    typedef __attribute__((address_space(3))) const void* lds_cptr;
+    return (uint32_t)(uintptr_t)(lds_cptr)p;
+}
+
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l's bytes at g land at LDS byte m0 + 16 l,
+// m0 wave-uniform. The load is written as inline asm so that the compiler
+// does not track it: once it sees such a load in flight, it waits for every
+// outstanding vector-memory instruction before any LDS read, which leaves no
+// load in flight across a computation. The caller therefore orders the bytes
+// itself: wait_vmcnt<N>() before the first LDS read of them, N counting every
+// vector-memory instruction (load or store) issued after this one, and no
+// store outstanding from before it (stores may complete out of order with
+// loads). M0 is restored; the one wait state between writing M0 and the load
+// reading it is the s_nop.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t m0) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(m0)
+        : "memory");
+}
+
+// s_waitcnt vmcnt(N): at most N vector-memory instructions of this wave left
+// in flight. A compiler barrier for memory accesses as well.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit count");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 constexpr int kQTileK = 8192;                // k per LDS tile (32 super-blocks)
 constexpr int kQSbPerTile = kQTileK / 256;
@@ -97,7 +138,7 @@ __device__ __forceinline__ void q6_stage_tile(Q6Lds<R>& L, const uint8_t* q8, in
     }
 }
 
-template <int R, int T, int WAVES, int MAXB, int BPC, int PF>
+template <int R, int T, int WAVES, int MAXB, int BPC>
 __global__ void __launch_bounds__(WAVES * kWave, (WAVES * BPC + 3) / 4)
 q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ q8, int H, int V,
                 uint16_t* __restrict__ out, int nsuper) {
@@ -108,11 +149,11 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     static_assert(NP <= 64 && R <= 8, "T*R must be <= 64, R <= 8");
     static_assert(kItemBytes + 15 <= 64 * 16, "an item must fit one 16-byte load per lane");
     static_assert((kItemBytes + 13) / 16 + 2 <= 61, "the shifted chunks stay in the row's buffer");
+    static_assert(T <= 63, "vmcnt counts the loads of one item");
     __shared__ Q6Lds<R> L;
     // wave-private weight staging, two buffers: [wave][item parity][row t]
-    // [1024 bytes]. Item it + 1 is written into one buffer at the start of
-    // step it, while item it is read from the other, so a whole step
-    // separates each item's LDS write from its reads.
+    // [1024 bytes]. Item it + 1 is loaded into one buffer at the start of
+    // step it, while item it is read from the other.
     __shared__ u32x4_t WB[WAVES][2][T][kWave];
 
     const int lane = threadIdx.x & 63;
@@ -153,6 +194,7 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     const int p_sc = p_sb + 192 + t16;
     const int p_d = p_sb + 208;
     const uint8_t* const wb = reinterpret_cast<const uint8_t*>(&WB[0][0][0]);
+    const uint32_t wb_lds = __builtin_amdgcn_readfirstlane(lds_byte_offset(&WB[wave][0][0][0]));
     // An item's first byte is 2-byte aligned, and its position mod 4 in the
     // staging buffer depends only on the parity of its vocab row: items start
     // at multiples of 840 bytes within a row, rows are hidden/256 x 210 bytes
@@ -195,66 +237,56 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
             const int nitems = nbb * nseg;
 
             // First byte of item (bi, s) in row t (rows past the vocab tail
-            // re-read the last row, never stored). Kept as a pointer into
-            // `blocks` so the loads stay global (not flat) loads.
+            // re-read the last row, never stored).
             auto item_ptr = [&](int bi, int s, int t) -> const uint8_t* {
                 const int v = min(((sj * MAXB + bi) * TW + gw) * T + t, V - 1);
                 const int sb0 = tt * kQSbPerTile + s * 4;
                 return blocks + (size_t)v * rowbytes + (size_t)sb0 * kQ6KBlockBytes;
             };
-            // One 16-byte aligned chunk per lane; lanes past the item's last
-            // chunk re-read it.
-            auto issue = [&](int bi, int s, u32x4_t (&g)[T]) {
+            // One 16-byte aligned chunk per lane and row into LDS buffer
+            // `buf`, lane l's chunk to slot l. Slot j holds chunk j, from slot
+            // 28 on chunk j - 2: super-blocks 2 and 3 (item bytes >= 420 +
+            // 0..14) land 32 bytes later, and slots 26 and 27 keep the tail
+            // of super-block 1 (bytes < 434). The last chunk an item needs is
+            // 53 (slot 55); the lanes past it load the item's last chunk
+            // again, into slots no lane reads.
+            const int lchunk = lane < 28 ? lane : lane - 2;
+            auto issue = [&](int bi, int s, int buf) __attribute__((always_inline)) {
                 const int sb0 = tt * kQSbPerTile + s * 4;
                 const int nbytes = min(4, nsb - sb0) * kQ6KBlockBytes;
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
                     const uint8_t* p = item_ptr(bi, s, t);
                     const int mis = (int)(reinterpret_cast<uintptr_t>(p) & 15);
-                    const uint8_t* p16 = p - mis;
-                    const int ch = min(lane, (mis + nbytes - 1) >> 4);
-                    g[t] = *reinterpret_cast<const u32x4_t*>(p16 + 16 * ch);
-                }
-            };
-            // Chunk j goes to slot j, from chunk 26 on to slot j + 2: super-
-            // blocks 2 and 3 (item bytes >= 420 + 0..14) land 32 bytes
-            // later. Chunks 26 and 27 also keep slot j for the tail of
-            // super-block 1 (bytes < 434). The last chunk an item needs is
-            // 53 (slot 55); lanes 62 and 63 hold copies of it and write
-            // nothing.
-            const int sslot = lane < 26 ? lane : lane + 2;
-            auto stage = [&](const u32x4_t (&g)[T], int buf) {
-#pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    if (lane < 62) WB[wave][buf][t][sslot] = g[t];
-                    if (lane == 26 || lane == 27) WB[wave][buf][t][lane] = g[t];
+                    const int ch = min(lchunk, (mis + nbytes - 1) >> 4);
+                    lds_dma16(p - mis + 16 * ch, wb_lds + (uint32_t)((buf * T + t) * kWave * 16));
                 }
             };
 
             float acc[NP];
             int bi = 0, s = 0;
-            // Ring of PF items: slot it % PF holds item it's chunks from its
-            // issue (PF - 1 steps ahead) until step it - 1 writes them to LDS
-            // buffer it & 1; step it then computes item it from that buffer,
-            // with items it + 2 .. it + PF in flight. The issue position
-            // (pbi, ps) stops at the last item.
-            u32x4_t gr[PF][T];
-            int pbi = 0, ps = 0, pit = 0;
-            auto next_issue = [&]() {
-                if (pit + 1 < nitems) {
-                    ++pit;
-                    if (++ps == nseg) {
-                        ps = 0;
-                        ++pbi;
-                    }
+            // (pbi, ps): the next item to load. Step it loads item it + 1 into
+            // the buffer that step it - 1 read (all its reads were consumed
+            // there), then waits for item it: T loads (item it + 1's) may
+            // stay in flight, none once the last item is loaded. Nothing else
+            // in this loop touches vector memory, and no store is in flight
+            // when it starts (the wait below), so the count is exact.
+            int pbi = 0, ps = 0;
+            auto load_next = [&](int buf) __attribute__((always_inline)) {
+                issue(pbi, ps, buf);
+                if (++ps == nseg) {
+                    ps = 0;
+                    ++pbi;
                 }
             };
-            auto step = [&](auto sl_tag, int it) __attribute__((always_inline)) {
-                constexpr int SL = decltype(sl_tag)::value;
-                constexpr int buf = SL & 1;
-                if (it + 1 < nitems) stage(gr[(SL + 1) % PF], buf ^ 1);
-                issue(pbi, ps, gr[SL]);
-                next_issue();
+            auto step = [&](int it) __attribute__((always_inline)) {
+                const int buf = it & 1;
+                if (it + 1 < nitems) {
+                    load_next(buf ^ 1);
+                    wait_vmcnt<T>();
+                } else {
+                    wait_vmcnt<0>();
+                }
                 if (s == 0) {
 #pragma unroll
                     for (int i = 0; i < NP; ++i) acc[i] = 0.0f;
@@ -329,22 +361,11 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                 }
             };
             if (nitems > 0) {
-#pragma unroll
-                for (int i = 0; i < PF; ++i) {
-                    issue(pbi, ps, gr[i]);
-                    next_issue();
-                }
-                stage(gr[0], 0);
+                wait_vmcnt<0>();  // the previous band group's logit stores
+                load_next(0);
             }
-            int it = 0;
 #pragma unroll 1
-            for (; it + PF <= nitems; it += PF)
-                static_for<PF>([&](auto sl) __attribute__((always_inline)) {
-                    step(sl, it + decltype(sl)::value);
-                });
-            static_for<PF>([&](auto sl) __attribute__((always_inline)) {
-                if (it + decltype(sl)::value < nitems) step(sl, it + decltype(sl)::value);
-            });
+            for (int it = 0; it < nitems; ++it) step(it);
         }
 
 #pragma unroll
@@ -356,7 +377,7 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     }
 }
 
-template <int R, int T, int WAVES, int MAXB, int BPC, int PF>
+template <int R, int T, int WAVES, int MAXB, int BPC>
 static hipError_t launch_q6k(const uint8_t* blocks, const uint8_t* q8, int H, int V,
                              uint16_t* out, const DeviceInfo& dev, hipStream_t stream) {
     const int64_t NB = (V + T - 1) / T;
@@ -365,7 +386,7 @@ static hipError_t launch_q6k(const uint8_t* blocks, const uint8_t* q8, int H, in
     const int64_t TW = nblk * WAVES;
     const int64_t per_wave = (NB + TW - 1) / TW;
     const int nsuper = (int)((per_wave + MAXB - 1) / MAXB);
-    hipLaunchKernelGGL((q6k_gemv_kernel<R, T, WAVES, MAXB, BPC, PF>), dim3((unsigned)nblk),
+    hipLaunchKernelGGL((q6k_gemv_kernel<R, T, WAVES, MAXB, BPC>), dim3((unsigned)nblk),
                        dim3(WAVES * kWave), 0, stream, blocks, q8, H, V, out, nsuper);
     return hipGetLastError();
 }
@@ -375,12 +396,12 @@ hipError_t run_q6k(const uint8_t* blocks, const uint8_t* q8, int R, int H, int V
     switch (R) {
 #define QH_Q6_CASE(RR, TT, WV, MB, BPC) \
     case RR:                            \
-        return launch_q6k<RR, TT, WV, MB, BPC, 2>(blocks, q8, H, V, out, dev, stream);
+        return launch_q6k<RR, TT, WV, MB, BPC>(blocks, q8, H, V, out, dev, stream);
         QH_Q6_CASE(1, 4, 8, 12, 2)
         QH_Q6_CASE(2, 2, 12, 8, 2)
-        QH_Q6_CASE(3, 2, 16, 12, 1)
-        QH_Q6_CASE(4, 2, 16, 12, 1)
-        QH_Q6_CASE(5, 4, 8, 12, 1)
+        QH_Q6_CASE(3, 4, 12, 12, 1)
+        QH_Q6_CASE(4, 4, 12, 12, 1)
+        QH_Q6_CASE(5, 4, 12, 12, 1)
         QH_Q6_CASE(6, 4, 8, 12, 1)
         QH_Q6_CASE(7, 4, 8, 12, 1)
         QH_Q6_CASE(8, 4, 8, 12, 1)
