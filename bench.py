@@ -81,7 +81,7 @@ class Workload:
 _W002 = "synthetic (seeded N(0,0.02) weights quantized on the device, N(0,1) BF16 x)"
 _FP8_SRC = ("fp8_gemv.hip", "qhead_device.h")
 _FP8_DTYPE = "fp8e4m3 x bf16 -> f32 acc, bf16 out"
-_W8_SRC = ("w8a8_gemv.hip", "act_quant.hip", "quant_common.h", "qhead_device.h")
+_W8_SRC = ("w8a8_gemv.hip", "act_quant.hip", "quant_common.h", "qhead_device.h", "lds_dma.h")
 WORKLOADS = {
     "fp8": Workload(
         synth.FP8_155136X8192, "1,2,4,8,16", "fp8_gemv_kernel", _FP8_SRC,
@@ -121,14 +121,14 @@ WORKLOADS = {
         "e2m1 x e4m3 block scale x bf16 -> f32 acc, bf16 out", _W002),
     "q6k": Workload(
         synth.NVFP4_Q6K_129280X7168, "1,2,4,8", "q6k_gemv_kernel + quant_q8_1_kernel (per call)",
-        ("q6k_gemv.hip", "act_quant.hip", "quant_common.h", "qhead_device.h"),
+        ("q6k_gemv.hip", "act_quant.hip", "quant_common.h", "qhead_device.h", "lds_dma.h"),
         "q6k_gemv_129280x7168_counters.json",
         "achieved HBM GB/s, Q6_K head 129280x7168 with q8_1 activations, rows 1..8",
         "int6 x int8 -> i32 dot4, f32 scales, bf16 out", _W002),
     "w8a8_silu": Workload(
         synth.SILU_DOWN_7168X18432, "1,16,128",
         "w8a8_valu_split_kernel / w8a8_mfma_kernel + silu_slice_max/quant kernels (per call)",
-        ("w8a8_gemv.hip", "silu_quant.hip", "quant_common.h", "qhead_device.h"),
+        ("w8a8_gemv.hip", "silu_quant.hip", "quant_common.h", "qhead_device.h", "lds_dma.h"),
         "w8a8_silu_7168x18432_counters.json",
         "achieved HBM GB/s, W8A8 SiLU down projection 7168x18432, calls of 1/16/128 rows",
         "bf16 silu(gate)*up -> fp8e4m3 x fp8e4m3 -> f32 acc, bf16 out",

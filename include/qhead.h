@@ -129,8 +129,10 @@ int qhead_quant_act_e4m3(const uint16_t* x_bf16, int32_t rows, int32_t hidden, u
 
 /* Bytes of workspace qhead_w8a8 and qhead_w8a8_silu need for `hidden`: the
  * quantized activations and scales of one 128-row chunk (W8a8Scratch of
- * "w8a8_layer.rs", sized by max_k and W8A8_MAX_ROWS) and 32 KiB of per-slice
- * maxima for the SiLU path, 256-byte aligned parts. 0 for hidden <= 0. */
+ * "w8a8_layer.rs", sized by max_k and W8A8_MAX_ROWS), 32 KiB of per-slice
+ * maxima for the SiLU path and the chunk's activations staged as BF16 for
+ * the GEMV (64 KiB per 256 of hidden), 256-byte aligned parts. 0 for
+ * hidden <= 0. */
 size_t qhead_w8a8_workspace_bytes(int32_t hidden);
 
 /* FP8 GEMV over already-quantized activations (the second step of W8A8,

@@ -159,8 +159,32 @@ int qhead_quant_act_e4m3(const uint16_t* x_bf16, int32_t rows, int32_t hidden, u
 size_t qhead_w8a8_workspace_bytes(int32_t hidden) {
     if (hidden <= 0) return 0;
     return align256((size_t)128 * hidden) + align256(128 * sizeof(float)) +
-           align256((size_t)128 * kSiluMaxSlices * sizeof(uint32_t));
+           align256((size_t)128 * kSiluMaxSlices * sizeof(uint32_t)) +
+           align256(w8a8_image_bytes(hidden));
 }
+
+// The W8A8 workspace: quantized activations, their scales, the SiLU per-slice
+// maxima, then the staged-activation image of the GEMV.
+namespace {
+struct W8a8Workspace {
+    uint8_t* xq;
+    float* sa;
+    uint32_t* maxbuf;
+    void* image;
+};
+W8a8Workspace w8a8_workspace_parts(void* workspace, int32_t hidden) {
+    W8a8Workspace w;
+    uint8_t* p = static_cast<uint8_t*>(workspace);
+    w.xq = p;
+    p += align256((size_t)128 * hidden);
+    w.sa = reinterpret_cast<float*>(p);
+    p += align256(128 * sizeof(float));
+    w.maxbuf = reinterpret_cast<uint32_t*>(p);
+    p += align256((size_t)128 * kSiluMaxSlices * sizeof(uint32_t));
+    w.image = p;
+    return w;
+}
+}  // namespace
 
 int qhead_w8a8_gemv(const uint8_t* w_e4m3, const float* row_scale, const uint8_t* xq,
                     const float* xscale, int32_t rows, int32_t hidden, int32_t vocab,
@@ -178,7 +202,8 @@ int qhead_w8a8_gemv(const uint8_t* w_e4m3, const float* row_scale, const uint8_t
     for (int32_t done = 0; done < rows;) {
         const int32_t m = (rows - done) < chunk ? (rows - done) : chunk;
         hipError_t e = run_w8a8_gemv(w_e4m3, row_scale, xq + (size_t)done * hidden, xscale + done,
-                                     m, hidden, vocab, out_bf16 + (size_t)done * vocab, dev, s);
+                                     m, hidden, vocab, out_bf16 + (size_t)done * vocab, dev, s,
+                                     nullptr);
         if (e != hipSuccess) return QHEAD_ERR_HIP;
         done += m;
     }
@@ -200,15 +225,14 @@ int qhead_w8a8(const uint8_t* w_e4m3, const float* row_scale, const uint16_t* x_
     DeviceInfo dev;
     if (int st = device_or_error(&dev)) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    uint8_t* xq = static_cast<uint8_t*>(workspace);
-    float* sa = reinterpret_cast<float*>(xq + align256((size_t)128 * hidden));
+    const W8a8Workspace w = w8a8_workspace_parts(workspace, hidden);
     for (int32_t done = 0; done < rows;) {
         const int32_t m = (rows - done) < max_rows(QHEAD_FMT_W8A8) ? (rows - done)
                                                                   : max_rows(QHEAD_FMT_W8A8);
-        hipError_t e = run_quant_act_e4m3(x_bf16 + (size_t)done * hidden, m, hidden, xq, sa, s);
+        hipError_t e = run_quant_act_e4m3(x_bf16 + (size_t)done * hidden, m, hidden, w.xq, w.sa, s);
         if (e != hipSuccess) return QHEAD_ERR_HIP;
-        e = run_w8a8_gemv(w_e4m3, row_scale, xq, sa, m, hidden, vocab,
-                          out_bf16 + (size_t)done * vocab, dev, s);
+        e = run_w8a8_gemv(w_e4m3, row_scale, w.xq, w.sa, m, hidden, vocab,
+                          out_bf16 + (size_t)done * vocab, dev, s, w.image);
         if (e != hipSuccess) return QHEAD_ERR_HIP;
         done += m;
     }
@@ -256,19 +280,16 @@ int qhead_w8a8_silu(const uint8_t* w_e4m3, const float* row_scale, const uint16_
     DeviceInfo dev;
     if (int st = device_or_error(&dev)) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    uint8_t* xq = static_cast<uint8_t*>(workspace);
-    float* sa = reinterpret_cast<float*>(xq + align256((size_t)128 * hidden));
-    uint32_t* maxbuf =
-        reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(sa) + align256(128 * sizeof(float)));
+    const W8a8Workspace w = w8a8_workspace_parts(workspace, hidden);
     for (int32_t done = 0; done < rows;) {
         const int32_t m = (rows - done) < max_rows(QHEAD_FMT_W8A8) ? (rows - done)
                                                                   : max_rows(QHEAD_FMT_W8A8);
         const size_t off = (size_t)done * ld;
-        hipError_t e = run_quant_act_silu_e4m3_split(gate + off, up + off, ld, m, hidden, xq, sa,
-                                                     maxbuf, s);
+        hipError_t e = run_quant_act_silu_e4m3_split(gate + off, up + off, ld, m, hidden, w.xq,
+                                                     w.sa, w.maxbuf, s);
         if (e != hipSuccess) return QHEAD_ERR_HIP;
-        e = run_w8a8_gemv(w_e4m3, row_scale, xq, sa, m, hidden, vocab,
-                          out_bf16 + (size_t)done * vocab, dev, s);
+        e = run_w8a8_gemv(w_e4m3, row_scale, w.xq, w.sa, m, hidden, vocab,
+                          out_bf16 + (size_t)done * vocab, dev, s, w.image);
         if (e != hipSuccess) return QHEAD_ERR_HIP;
         done += m;
     }

@@ -32,49 +32,11 @@
 // registers between issue and use. The -32 offset is folded into the
 // integer dot: the staging step stores -32 * sum(q8) per sub-block next to
 // the q8 values.
+#include "lds_dma.h"
 #include "qhead_device.h"
 #include "qhead_internal.h"
 
 namespace qh {
-
-// Byte offset of an LDS object within the workgroup's LDS allocation: the
-// value M0 takes for a load straight into LDS.
-__device__ __forceinline__ uint32_t lds_byte_offset(const void* p) {
-    typedef __attribute__((address_space(3))) const void* lds_cptr;
-    return (uint32_t)(uintptr_t)(lds_cptr)p;
-}
-
-// 16 bytes per lane from global memory straight into LDS
-// (global_load_lds_dwordx4): lane l's bytes at g land at LDS byte m0 + 16 l,
-// m0 wave-uniform. The load is written as inline asm so that the compiler
-// does not track it: once it sees such a load in flight, it waits for every
-// outstanding vector-memory instruction before any LDS read, which leaves no
-// load in flight across a computation. The caller therefore orders the bytes
-// itself: wait_vmcnt<N>() before the first LDS read of them, N counting every
-// vector-memory instruction (load or store) issued after this one, and no
-// store outstanding from before it (stores may complete out of order with
-// loads). M0 is restored; the one wait state between writing M0 and the load
-// reading it is the s_nop.
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t m0) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(g), "s"(m0)
-        : "memory");
-}
-
-// s_waitcnt vmcnt(N): at most N vector-memory instructions of this wave left
-// in flight. A compiler barrier for memory accesses as well.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit count");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 constexpr int kQTileK = 8192;                // k per LDS tile (32 super-blocks)
 constexpr int kQSbPerTile = kQTileK / 256;
@@ -269,8 +231,7 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
             // the buffer that step it - 1 read (all its reads were consumed
             // there), then waits for item it: T loads (item it + 1's) may
             // stay in flight, none once the last item is loaded. Nothing else
-            // in this loop touches vector memory, and no store is in flight
-            // when it starts (the wait below), so the count is exact.
+            // in this loop loads from vector memory, so the count is exact.
             int pbi = 0, ps = 0;
             auto load_next = [&](int buf) __attribute__((always_inline)) {
                 issue(pbi, ps, buf);
@@ -360,10 +321,7 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                     ++s;
                 }
             };
-            if (nitems > 0) {
-                wait_vmcnt<0>();  // the previous band group's logit stores
-                load_next(0);
-            }
+            if (nitems > 0) load_next(0);
 #pragma unroll 1
             for (int it = 0; it < nitems; ++it) step(it);
         }

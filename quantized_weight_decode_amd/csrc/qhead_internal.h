@@ -21,7 +21,9 @@ hipError_t run_fp8_w8a16(const uint8_t* W, const float* s, const uint16_t* x, in
 // W8A8 GEMV over quantized activations (1 <= R <= 128 rows per launch).
 hipError_t run_w8a8_gemv(const uint8_t* W, const float* sw, const uint8_t* xq, const float* sa,
                          int R, int H, int V, uint16_t* out, const DeviceInfo& dev,
-                         hipStream_t stream);
+                         hipStream_t stream, void* image);
+// Bytes of the staged-activation image run_w8a8_gemv may use for `H`.
+size_t w8a8_image_bytes(int H);
 
 // Activation quantizers and weight preparation.
 hipError_t run_quant_act_e4m3(const uint16_t* x, int rows, int H, uint8_t* xq, float* sa,

@@ -27,6 +27,7 @@
 // Eight chains keep the VALU kernel's weight reads in 128-byte runs per row
 // (8 lanes x 16 bytes), which stream near the rate of longer runs, while the
 // MFMA kernel holds 8 chains x 8 row tiles of accumulators at 128 rows.
+#include "lds_dma.h"
 #include "qhead_device.h"
 #include "qhead_internal.h"
 
@@ -560,11 +561,47 @@ hipError_t launch_valu_split(const uint8_t* W, const float* ws, const uint8_t* x
 // loads measured faster. At the end of each 4096-k tile the chains go
 // through the tree (across the waves of a tile through LDS) and restart
 // from zero.
-template <int RT, int VTW, int CS, int PF, int LW>
+// The staged activations come either from the E4M3 codes, loaded two slabs
+// ahead and converted and written by the workgroup while the previous slab
+// computes, or (IMG = 1, direct weight loads) from an image of every slab's
+// staged bytes built once per call (w8a8_image_kernel), copied into LDS by
+// 16-byte loads that bypass the registers (global_load_lds_dwordx4): the
+// conversion, the LDS writes and their registers leave the slab loop. Both
+// stage the same bytes, so the results are bit-identical.
+template <int RT>
+__global__ void __launch_bounds__(256)
+w8a8_image_kernel(const uint8_t* __restrict__ xq, int R, int H, uint4* __restrict__ img, int NS) {
+    // One (slab, chain X, row r) unit per thread: slab s's image holds at
+    // X * 4 * RP + g * RP + ((r & ~15) | ((r + X) & 15)) the 16 bytes that
+    // the kernel below stages there (rows >= R and columns >= H as zero).
+    constexpr int RP = 16 * RT;
+    constexpr int UNITS = kChains * RP;
+    constexpr int SLAB_VEC = kChains * 4 * RP;
+    const int idx = (int)(blockIdx.x * 256 + threadIdx.x);
+    const int s = idx / UNITS;
+    if (s >= NS) return;
+    const int u = idx - s * UNITS;
+    const int X = u % kChains;
+    const int r = u / kChains;
+    const int ka = s * kSlabK + X * kGranK;
+    const int kb = ka + kStepK;
+    uint4 ca = make_uint4(0, 0, 0, 0), cb = make_uint4(0, 0, 0, 0);
+    if (r < R && ka < H) ca = *reinterpret_cast<const uint4*>(xq + (size_t)r * H + ka);
+    if (r < R && kb < H) cb = *reinterpret_cast<const uint4*>(xq + (size_t)r * H + kb);
+    uint32_t pa[8], pb[8];
+    e4m3x16_to_bf16(ca, pa);
+    e4m3x16_to_bf16(cb, pb);
+    uint4* dst = img + (size_t)s * SLAB_VEC + X * 4 * RP + ((r & ~15) | ((r + X) & 15));
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) dst[gg * RP] = make_uint4(pa[gg], pa[4 + gg], pb[gg], pb[4 + gg]);
+}
+
+template <int RT, int VTW, int CS, int PF, int LW, int IMG>
 __global__ void __launch_bounds__(VTW * CS * kWave, (VTW * CS + 3) / 4)
 w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale,
-                 const uint8_t* __restrict__ xq, const float* __restrict__ xscale, int R, int H,
-                 int V, uint16_t* __restrict__ out, int nrounds) {
+                 const uint8_t* __restrict__ xq, const uint4* __restrict__ img,
+                 const float* __restrict__ xscale, int R, int H, int V,
+                 uint16_t* __restrict__ out, int nrounds) {
     constexpr int WAVES = VTW * CS;
     constexpr int RP = 16 * RT;
     constexpr int NTHREADS = WAVES * kWave;
@@ -580,6 +617,12 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
     static_assert(PF % 2 == 0, "the staging slots follow the slab parity");
     // the tree's exchange reuses a slab buffer: (CS - 1) partial sums per tile
     static_assert((CS - 1) * VTW * RT * kWave <= SLAB_VEC, "exchange fits a slab buffer");
+    // IMG: 16-byte loads straight into LDS per lane and slab (each wave a
+    // contiguous 1 KiB run per load); every weight piece of a slab is
+    // converted before they are issued.
+    constexpr int DPT = SLAB_VEC / NTHREADS;
+    static_assert(!IMG || (LW == 0 && SLAB_VEC % NTHREADS == 0 && NCW <= 4),
+                  "image staging: direct weight loads, whole loads per wave");
     __shared__ uint4 xs[2][SLAB_VEC];
     __shared__ uint4 wl[LW ? 2 : 1][LW ? VTW * 16 * 16 : 1];
     __shared__ float xsc[RP];
@@ -734,13 +777,25 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
             ++rd;
         }
     };
-    stage_load(0, st[0]);
-    stage_write(0, st[0], xs[0]);
-    if (sit + 1 < total) {
-        ++sit;
-        ss = ss + 1 == NS ? 0 : ss + 1;
+    // IMG: wave w loads uint4 [(w * DPT + j) * 64, + 64) of each slab's
+    // image, lane l one of them, into the same place of the slab buffer.
+    const uint4* img_w = img + (size_t)(wave * DPT) * kWave + lane;
+    const uint32_t xs_lds = IMG ? __builtin_amdgcn_readfirstlane(lds_byte_offset(&xs[0][0])) : 0u;
+    auto img_dst = [&](int buf, int j) {
+        return xs_lds + (uint32_t)((buf * SLAB_VEC + (wave * DPT + j) * kWave) * 16);
+    };
+    if constexpr (IMG) {
+#pragma unroll
+        for (int j = 0; j < DPT; ++j) lds_dma16(img_w + j * kWave, img_dst(0, j));
+    } else {
+        stage_load(0, st[0]);
+        stage_write(0, st[0], xs[0]);
+        if (sit + 1 < total) {
+            ++sit;
+            ss = ss + 1 == NS ? 0 : ss + 1;
+        }
+        stage_load(ss * kSlabK, st[1]);
     }
-    stage_load(ss * kSlabK, st[1]);
     const uint8_t* wrow = W + (size_t)row_of(0) * H;
     // The weights PF - 1 slabs ahead: position advance and load.
     auto wnext = [&]() {
@@ -764,6 +819,7 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
     }
     if constexpr (LW) wstage(wb[0], wl[0]);
     const float* swp = wscale + row_of(0);
+    if constexpr (IMG) wait_vmcnt<0>();
     __syncthreads();
 
     // One slab: SL = it % PF (a compile-time slot, the loop is unrolled by PF).
@@ -785,13 +841,15 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
         read_a(0);
         // Activation codes two slabs ahead (their slot held this slab's
         // codes, already in LDS), then the weights PF - 1 slabs ahead.
-        if (sit + 1 < total) {
-            ++sit;
-            ss = ss + 1 == NS ? 0 : ss + 1;
+        if constexpr (!IMG) {
+            if (sit + 1 < total) {
+                ++sit;
+                ss = ss + 1 == NS ? 0 : ss + 1;
+            }
+            stage_load(ss * kSlabK, st[SL % 2]);
+            wissue(wb[(SL + PF - 1) % PF]);
+            wnext();
         }
-        stage_load(ss * kSlabK, st[SL % 2]);
-        wissue(wb[(SL + PF - 1) % PF]);
-        wnext();
         // This slab's weight pieces: from LDS (staged in the previous slab)
         // or the load ring.
         uint4 wv[NLW];
@@ -803,10 +861,30 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
         // This tile's row scale, loaded every slab so that no load sits in
         // the branch that stores (a load there stalls the prefetches above).
         const float sw = *swp;
-        // The next slab's activations into the other buffer (read by every
-        // wave in the previous slab, before its barrier); its conversion
-        // overlaps this slab's MFMAs.
-        if (more) {
+        // This slab's weight pieces as BF16 pairs (cw[j] from piece j).
+        uint32_t cw[NLW][8];
+        if constexpr (IMG) {
+            // IMG: the pieces are converted first, so that the compiler's
+            // wait for them comes before the next slab's image loads (the
+            // first of which takes the last converted word as an input);
+            // a wait placed after those loads would also wait for them.
+            // The image loads then fill the other buffer (read by every
+            // wave in the previous slab, before its barrier) while this
+            // slab's MFMAs run, followed by the weights PF - 1 slabs ahead.
+#pragma unroll
+            for (int j = 0; j < NLW; ++j) e4m3x16_to_bf16(wv[j], cw[j]);
+            if (more) {
+                const uint4* src = img_w + (size_t)(s + 1 == NS ? 0 : s + 1) * SLAB_VEC;
+                lds_dma16_after(src, img_dst((SL + 1) & 1, 0), cw[NLW - 1][7]);
+#pragma unroll
+                for (int j = 1; j < DPT; ++j) lds_dma16(src + j * kWave, img_dst((SL + 1) & 1, j));
+            }
+            wissue(wb[(SL + PF - 1) % PF]);
+            wnext();
+        } else if (more) {
+            // The next slab's activations into the other buffer (read by
+            // every wave in the previous slab, before its barrier); its
+            // conversion overlaps this slab's MFMAs.
             stage_write((s + 1 == NS ? 0 : s + 1) * kSlabK, st[(SL + 1) % 2], xs[(SL + 1) & 1]);
             if constexpr (LW) wstage(wb[(SL + 1) % PF], wl[(SL + 1) & 1]);
         }
@@ -830,9 +908,12 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
             for (int j = 0; j < NCW / 4; ++j) {
                 // Four chains: a1[Q] = pair g of granule A of chain Q's row,
                 // a1[4+Q] its pair 4+g; a2[] the same for granule B.
-                uint32_t a1[8], a2[8];
-                e4m3x16_to_bf16(wv[2 * j], a1);
-                e4m3x16_to_bf16(wv[2 * j + 1], a2);
+                uint32_t(&a1)[8] = cw[2 * j];
+                uint32_t(&a2)[8] = cw[2 * j + 1];
+                if constexpr (!IMG) {
+                    e4m3x16_to_bf16(wv[2 * j], a1);
+                    e4m3x16_to_bf16(wv[2 * j + 1], a2);
+                }
                 xpose4(a1[0], a1[1], a1[2], a1[3]);
                 xpose4(a1[4], a1[5], a1[6], a1[7]);
                 xpose4(a2[0], a2[1], a2[2], a2[3]);
@@ -845,8 +926,8 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
             for (int j = 0; j < NCW / 2; ++j) {
                 // Chains 2j, 2j+1: o[Q] holds pair g of granule Q's row
                 // (Q = 2c + granule), o[4 + Q] its pair 4 + g.
-                uint32_t o[8];
-                e4m3x16_to_bf16(wv[j], o);
+                uint32_t(&o)[8] = cw[j];
+                if constexpr (!IMG) e4m3x16_to_bf16(wv[j], o);
                 xpose4(o[0], o[1], o[2], o[3]);
                 xpose4(o[4], o[5], o[6], o[7]);
 #pragma unroll
@@ -931,6 +1012,9 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
         }
         adv(cs, cround);
         if (cs == 0) swp = wscale + row_of(cround);
+        // IMG: the next slab's image has landed once nothing is in flight
+        // (the weight loads issued after it are waited for too).
+        if constexpr (IMG) wait_vmcnt<0>();
         __syncthreads();
     };
 
@@ -945,25 +1029,53 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
     });
 }
 
-template <int RT, int VTW, int CS, int PF, int LW = 0>
+template <int RT, int VTW, int CS, int PF, int LW = 0, int IMG = 0>
 hipError_t launch_mfma(const uint8_t* W, const float* ws, const uint8_t* xq, const float* xs,
-                       int R, int H, int V, uint16_t* out, const DeviceInfo& dev,
+                       int R, int H, int V, uint16_t* out, void* image, const DeviceInfo& dev,
                        hipStream_t stream) {
     const int64_t ntiles = (V + 15) / 16;
     int64_t blocks = (ntiles + VTW - 1) / VTW;
     if (blocks > (int64_t)dev.num_cus) blocks = (int64_t)dev.num_cus;
     const int nrounds = (int)((ntiles + blocks * VTW - 1) / (blocks * VTW));
-    hipLaunchKernelGGL((w8a8_mfma_kernel<RT, VTW, CS, PF, LW>), dim3((unsigned)blocks),
-                       dim3(VTW * CS * kWave), 0, stream, W, ws, xq, xs, R, H, V, out, nrounds);
+    if constexpr (IMG) {
+        const int NS = (H + kSlabK - 1) / kSlabK;
+        const int n = NS * kChains * 16 * RT;
+        hipLaunchKernelGGL((w8a8_image_kernel<RT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                           stream, xq, R, H, static_cast<uint4*>(image), NS);
+    }
+    hipLaunchKernelGGL((w8a8_mfma_kernel<RT, VTW, CS, PF, LW, IMG>), dim3((unsigned)blocks),
+                       dim3(VTW * CS * kWave), 0, stream, W, ws, xq,
+                       static_cast<const uint4*>(image), xs, R, H, V, out, nrounds);
     return hipGetLastError();
+}
+
+// A shape with direct weight loads: through the image when the caller gives
+// room for one.
+template <int RT, int VTW, int CS, int PF>
+hipError_t launch_mfma_direct(const uint8_t* W, const float* ws, const uint8_t* xq, const float* xs,
+                              int R, int H, int V, uint16_t* out, void* image,
+                              const DeviceInfo& dev, hipStream_t stream) {
+    if (image)
+        return launch_mfma<RT, VTW, CS, PF, 0, 1>(W, ws, xq, xs, R, H, V, out, image, dev, stream);
+    return launch_mfma<RT, VTW, CS, PF, 0, 0>(W, ws, xq, xs, R, H, V, out, nullptr, dev, stream);
 }
 
 }  // namespace
 
-// One W8A8 launch of 1..128 rows.
+size_t w8a8_image_bytes(int H) {
+    // one 128-row slab image (8 chains x 4 lane groups x 128 rows x 16 bytes)
+    // per 256-k slab
+    return H <= 0 ? 0 : (size_t)((H + kSlabK - 1) / kSlabK) * kChains * 4 * 128 * 16;
+}
+
+// One W8A8 launch of 1..128 rows. `image` (nullable): device memory of
+// w8a8_image_bytes(H) bytes, 16-byte aligned, that the shapes with direct
+// weight loads (from 17 rows on heads of fewer than four vocab tiles per CU,
+// from 33 rows otherwise) fill with the staged BF16 activations and copy
+// from.
 hipError_t run_w8a8_gemv(const uint8_t* W, const float* sw, const uint8_t* xq, const float* sa,
                          int R, int H, int V, uint16_t* out, const DeviceInfo& dev,
-                         hipStream_t stream) {
+                         hipStream_t stream, void* image) {
     // Narrow projections (fewer than two bands of the kernel below per SIMD)
     // split the hidden dimension over the waves of a workgroup instead, when
     // its LDS (windows and tile sums) stays within 64 KiB.
@@ -1029,34 +1141,38 @@ hipError_t run_w8a8_gemv(const uint8_t* W, const float* sw, const uint8_t* xq, c
     if (ntiles < (int64_t)dev.num_cus * 4) {
         switch ((R + 15) / 16) {
             case 1:
-                return launch_mfma<1, 2, 4, 4, 1>(W, sw, xq, sa, R, H, V, out, dev, stream);
+                return launch_mfma<1, 2, 4, 4, 1>(W, sw, xq, sa, R, H, V, out, nullptr, dev,
+                                                  stream);
             case 2:
-                return launch_mfma<2, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
+                return launch_mfma_direct<2, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, image, dev,
+                                                      stream);
             case 3:
-                return launch_mfma<3, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
+                return launch_mfma_direct<3, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, image, dev,
+                                                      stream);
             case 4:
-                return launch_mfma<4, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
+                return launch_mfma_direct<4, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, image, dev,
+                                                      stream);
             default:
                 break;
         }
     }
     switch ((R + 15) / 16) {
         case 1:
-            return launch_mfma<1, 8, 1, 4, 1>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma<1, 8, 1, 4, 1>(W, sw, xq, sa, R, H, V, out, nullptr, dev, stream);
         case 2:
-            return launch_mfma<2, 8, 1, 4, 1>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma<2, 8, 1, 4, 1>(W, sw, xq, sa, R, H, V, out, nullptr, dev, stream);
         case 3:
-            return launch_mfma<3, 4, 2, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma_direct<3, 4, 2, 4>(W, sw, xq, sa, R, H, V, out, image, dev, stream);
         case 4:
-            return launch_mfma<4, 4, 2, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma_direct<4, 4, 2, 4>(W, sw, xq, sa, R, H, V, out, image, dev, stream);
         case 5:
-            return launch_mfma<5, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma_direct<5, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, image, dev, stream);
         case 6:
-            return launch_mfma<6, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma_direct<6, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, image, dev, stream);
         case 7:
-            return launch_mfma<7, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma_direct<7, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, image, dev, stream);
         default:
-            return launch_mfma<8, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, dev, stream);
+            return launch_mfma_direct<8, 2, 4, 4>(W, sw, xq, sa, R, H, V, out, image, dev, stream);
     }
 }
 

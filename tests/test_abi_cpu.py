@@ -70,6 +70,9 @@ def test_plan_chunks(qh):
 
 def test_workspace_sizes(qh):
     assert qh.w8a8_workspace_bytes(7168) >= 128 * 7168 + 128 * 4
+    # the GEMV's staged BF16 activations: 64 KiB per 256 of hidden
+    assert qh.w8a8_workspace_bytes(7168) >= 128 * 7168 + 28 * 65536
+    assert qh.w8a8_workspace_bytes(7169) >= qh.w8a8_workspace_bytes(7168) + 65536
     assert qh.w8a8_workspace_bytes(7168) % 256 == 0
     assert qh.w8a8_workspace_bytes(0) == 0
     assert qh.q6k_workspace_bytes(7168) >= 8 * (7168 // 32) * 36

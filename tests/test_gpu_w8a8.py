@@ -93,6 +93,28 @@ def test_w8a8_exact_cases_mfma_bit_exact(qh, R):
     assert np.array_equal(host_bits(out), oracle.bf16_rne_array(ref))
 
 
+@pytest.mark.parametrize("V,H", [(1001, 1040), (20000, 4112), (700, 8208), (37, 16)])
+def test_w8a8_staged_image_equals_in_kernel_staging(qh, V, H):
+    """qhead_w8a8 stages the activations of its launches with direct weight
+    loads from a BF16 image built in its workspace (copied into LDS without
+    passing through registers); qhead_w8a8_gemv, which has no workspace,
+    converts the codes inside the kernel. Both must stage the same bytes, so
+    on the same quantized activations their logits are bit-identical, at row
+    counts on every launch shape (narrow heads from 17 rows, wide heads from
+    33) including ragged row tiles."""
+    w, s = _head(V, H)
+    x = synth.activations_bf16(synth.W8A8_129280X7168, 128, hidden=H, max_rows=128)
+    wd, sd = dev_u8(w), dev_f32(s)
+    ws = qh.w8a8_workspace(H, DEV)
+    for R in (17, 32, 33, 40, 48, 49, 64, 65, 80, 97, 113, 128):
+        log(f"[case] w8a8 image vs in-kernel staging V={V} H={H} R={R}")
+        xd = dev_bf16(x[:R])
+        xq, sa = qh.quant_act_e4m3(xd)
+        staged = host_bits(qh.w8a8_gemv(wd, sd, xq, sa))
+        imaged = host_bits(qh.w8a8(wd, sd, xd, workspace=ws))
+        assert np.array_equal(imaged, staged), f"V={V} H={H} R={R}: image path differs"
+
+
 def test_w8a8_full_head_row_counts_across_kernels(qh):
     """The 129280 x 7168 head: rows of 1-, 4-, 15-, 16-, 17- and 128-row
     calls equal the same rows of the 300-row call (128 + 128 + 44), and the
