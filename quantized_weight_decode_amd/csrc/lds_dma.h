@@ -15,8 +15,9 @@ __device__ __forceinline__ uint32_t lds_byte_offset(const void* p) {
 }
 
 // 16 bytes per lane from global memory straight into LDS
-// (global_load_lds_dwordx4): lane l's bytes at g land at LDS byte m0 + 16 l,
-// m0 wave-uniform. The load is written as inline asm so that the compiler
+// (global_load_lds_dwordx4): lane l's bytes at base + voff land at LDS byte
+// m0 + 16 l, with base and m0 wave-uniform (SGPRs) and voff the lane's
+// 32-bit byte offset. The load is written as inline asm so that the compiler
 // does not track it: once it sees such a load in flight, it waits for every
 // outstanding vector-memory instruction before any LDS read, which leaves no
 // load in flight across a computation. The caller therefore orders the bytes
@@ -28,33 +29,21 @@ __device__ __forceinline__ uint32_t lds_byte_offset(const void* p) {
 // the wait longer. The compiler's own waits stay correct for the same
 // reason (the loads it does not see only make them longer), but a wait it
 // places after such a load also waits for it: issue these after the first
-// use of any register load that is still in flight. M0 is restored; the one
-// wait state between writing M0 and the load reading it is the s_nop.
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t m0) {
+// use of any register load still in flight, which `after`, a value computed
+// from that use, enforces (an asm input the instruction does not read). M0
+// is restored; the one wait state between writing M0 and the load reading
+// it is the s_nop.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t m0,
+                                          uint32_t after = 0u) {
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
+        "s_mov_b32 m0, %3\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "v"(g), "s"(m0)
-        : "memory");
-}
-
-// lds_dma16, issued only once `after` has been computed: a value computed from
-// a register load pins that load's wait ahead of this one.
-__device__ __forceinline__ void lds_dma16_after(const void* g, uint32_t m0, uint32_t after) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(g), "s"(m0), "v"(after)
+        : "v"(voff), "s"(base), "s"(m0), "v"(after)
         : "memory");
 }
 

@@ -220,8 +220,8 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                 for (int t = 0; t < T; ++t) {
                     const uint8_t* p = item_ptr(bi, s, t);
                     const int mis = (int)(reinterpret_cast<uintptr_t>(p) & 15);
-                    const int ch = min(lchunk, (mis + nbytes - 1) >> 4);
-                    lds_dma16(p - mis + 16 * ch, wb_lds + (uint32_t)((buf * T + t) * kWave * 16));
+                    const uint32_t ch = (uint32_t)min(lchunk, (mis + nbytes - 1) >> 4);
+                    lds_dma16(p - mis, 16u * ch, wb_lds + (uint32_t)((buf * T + t) * kWave * 16));
                 }
             };
 

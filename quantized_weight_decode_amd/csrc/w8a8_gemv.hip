@@ -778,15 +778,20 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
         }
     };
     // IMG: wave w loads uint4 [(w * DPT + j) * 64, + 64) of each slab's
-    // image, lane l one of them, into the same place of the slab buffer.
-    const uint4* img_w = img + (size_t)(wave * DPT) * kWave + lane;
+    // image, lane l one of them, into the same place of the slab buffer
+    // (wave-uniform base and LDS address, the lane's offset 16 l).
     const uint32_t xs_lds = IMG ? __builtin_amdgcn_readfirstlane(lds_byte_offset(&xs[0][0])) : 0u;
-    auto img_dst = [&](int buf, int j) {
-        return xs_lds + (uint32_t)((buf * SLAB_VEC + (wave * DPT + j) * kWave) * 16);
+    const uint32_t img_voff = (uint32_t)lane * 16u;
+    auto img_slab = [&](int sn, int buf, uint32_t after) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < DPT; ++j) {
+            const int v0 = (wave * DPT + j) * kWave;  // first uint4 of this run
+            lds_dma16(img + (size_t)sn * SLAB_VEC + v0, img_voff,
+                      xs_lds + (uint32_t)((buf * SLAB_VEC + v0) * 16), after);
+        }
     };
     if constexpr (IMG) {
-#pragma unroll
-        for (int j = 0; j < DPT; ++j) lds_dma16(img_w + j * kWave, img_dst(0, j));
+        img_slab(0, 0, 0u);
     } else {
         stage_load(0, st[0]);
         stage_write(0, st[0], xs[0]);
@@ -873,12 +878,7 @@ w8a8_mfma_kernel(const uint8_t* __restrict__ W, const float* __restrict__ wscale
             // slab's MFMAs run, followed by the weights PF - 1 slabs ahead.
 #pragma unroll
             for (int j = 0; j < NLW; ++j) e4m3x16_to_bf16(wv[j], cw[j]);
-            if (more) {
-                const uint4* src = img_w + (size_t)(s + 1 == NS ? 0 : s + 1) * SLAB_VEC;
-                lds_dma16_after(src, img_dst((SL + 1) & 1, 0), cw[NLW - 1][7]);
-#pragma unroll
-                for (int j = 1; j < DPT; ++j) lds_dma16(src + j * kWave, img_dst((SL + 1) & 1, j));
-            }
+            if (more) img_slab(s + 1 == NS ? 0 : s + 1, (SL + 1) & 1, cw[NLW - 1][7]);
             wissue(wb[(SL + PF - 1) % PF]);
             wnext();
         } else if (more) {
