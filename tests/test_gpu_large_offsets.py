@@ -38,20 +38,28 @@ def test_fp8_head_beyond_2gib(qh):
         blk = w[lo:lo + (1 << 15)]
         blk ^= ((blk & 0x7F) == 0x7F).to(torch.uint8)
     s = torch.rand(V, dtype=torch.float32, device=DEV, generator=gen) * 1e-3 + 1e-4
-    x = synth.activations_bf16(synth.FP8_155136X8192, R, max_rows=R)
-    out = qh.fp8_rowscale(w, s, dev_bf16(x))
-    out8 = qh.w8a8(w, s, dev_bf16(x))          # the W8A8 variant of the same kernel
+    x = synth.activations_bf16(synth.FP8_155136X8192, 40, max_rows=40)
+    out = qh.fp8_rowscale(w, s, dev_bf16(x[:R]))
+    out8 = qh.w8a8(w, s, dev_bf16(x[:R]))      # the W8A8 variant of the same kernel
+    # W8A8 on its MFMA kernel: 16 rows (weights through LDS) and 40 rows
+    # (direct weight loads, activations from the staged image)
+    out8_16 = qh.w8a8(w, s, dev_bf16(x[:16]))
+    out8_40 = qh.w8a8(w, s, dev_bf16(x))
     torch.cuda.synchronize()
     rows = _sample_rows(V, first_high)
     idx = torch.from_numpy(rows).to(DEV)
     w_h, s_h = w[idx].cpu().numpy(), s[idx].cpu().numpy()
     got, got8 = host_bits(out[:, idx]), host_bits(out8[:, idx])
+    got8_16, got8_40 = host_bits(out8_16[:, idx]), host_bits(out8_40[:, idx])
     del w
-    ref, ad = oracle.fp8_rowscale_ref(w_h, s_h, x)
+    ref, ad = oracle.fp8_rowscale_ref(w_h, s_h, x[:R])
     assert_within_bound(got, ref, ad, "fp8 beyond 2 GiB")
     xq, sa = oracle.quant_act_e4m3(x)
     ref8, ad8 = oracle.w8a8_ref(w_h, s_h, xq, sa)
-    assert_within_bound(got8, ref8, ad8, "w8a8 beyond 2 GiB")
+    assert_within_bound(got8, ref8[:R], ad8[:R], "w8a8 beyond 2 GiB")
+    assert_within_bound(got8_40, ref8, ad8, "w8a8 40 rows beyond 2 GiB")
+    assert np.array_equal(got8_16, got8_40[:16]), "w8a8 beyond 2 GiB: 16-row call differs"
+    assert np.array_equal(got8, got8_40[:R]), "w8a8 beyond 2 GiB: 3-row call differs"
 
 
 def test_q6k_head_beyond_2gib(qh):
