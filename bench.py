@@ -166,13 +166,11 @@ def compute_roof_us(name: str, V: int, H: int, R: int):
     rows must issue, at the chip's peak issue rate, from the kernels' inner
     loops per weight byte and pass (the rest -- trees, stores, quantizers --
     is left out, so this is a lower bound of the compute time):
-      FP8 W8A16, W8A8 on its VALU kernels (up to 8 rows; 10 on heads under
-        65536 vocab rows, which take the split VALU kernel): per BF16 pair of
-        weights one half-rate convert (2 lane-slots) and one v_dot2_f32_bf16
-        per row: (R + 2) / 2 lane-slots per weight byte;
-      W8A8 on its MFMA kernel (the rest, up to 128 rows per pass): 32 *
-        ceil(R / 16) 16x16x32 BF16 MFMAs per 16 vocab rows and 256 k, 16
-        cycles each on one of the 1024 SIMDs;
+      FP8 W8A16, W8A8 below 16 rows: per BF16 pair of weights one half-rate
+        convert (2 lane-slots) and one v_dot2_f32_bf16 per row: (R + 2) / 2
+        lane-slots per weight byte;
+      W8A8 at 16..128 rows: 32 * ceil(R / 16) 16x16x32 BF16 MFMAs per 16 vocab
+        rows and 256 k, 16 cycles each on one of the 1024 SIMDs;
       NVFP4: per byte (one pair) a 2-slot convert, R dot2 and R / 8 block FMAs,
         plus about 0.3 slots of block-scale decode: 2.3 + 1.125 R;
       Q6_K: per 16 weights 24 slots of 6-bit decode and scale, and per row
@@ -186,8 +184,7 @@ def compute_roof_us(name: str, V: int, H: int, R: int):
     chunks = [min(step, R - d) for d in range(0, R, step)]
     valu = mfma_cycles = 0.0
     for m in chunks:
-        w8a8_valu_max = 10 if V < 65536 else 8
-        if fmt in ("fp8", "w8a8") and not (fmt == "w8a8" and m > w8a8_valu_max):
+        if fmt in ("fp8", "w8a8") and not (fmt == "w8a8" and m >= 16):
             valu += V * H / 2 * (m + 2)
         elif fmt == "w8a8":
             mfma_cycles += -(-V // 16) * -(-H // 256) * 32 * -(-m // 16) * MFMA_16X16X32_CYCLES

@@ -7,11 +7,9 @@
 // depend on how many rows share the call ("w8a8_layer.rs" module doc).
 //
 // One arithmetic for every row count, served by two kernels:
-//  * up to 8 rows (10 on narrow heads): VALU kernel, one v_dot2_f32_bf16 per
-//    activation-weight pair;
-//  * above that, up to 128 rows: MFMA kernel, v_mfma_f32_16x16x32_bf16, one
-//    weight pass for all rows of the launch (in 16-row tiles, which cost the
-//    same for any row count up to 16).
+//  * 1..15 rows: VALU kernel, one v_dot2_f32_bf16 per activation-weight pair;
+//  * 16..128 rows: MFMA kernel, v_mfma_f32_16x16x32_bf16, one weight pass
+//    for all rows of the launch.
 // An MFMA of this shape adds the 8 products of each 16-lane group as one
 // step; when exactly one BF16 pair of a step is nonzero, the step rounds
 // exactly like v_dot2_f32_bf16 on that pair (checked bit for bit on the
@@ -1078,20 +1076,14 @@ size_t w8a8_image_bytes(int H) {
 hipError_t run_w8a8_gemv(const uint8_t* W, const float* sw, const uint8_t* xq, const float* sa,
                          int R, int H, int V, uint16_t* out, const DeviceInfo& dev,
                          hipStream_t stream, void* image) {
-    // Narrow projections (fewer than two bands of the VALU kernel per SIMD)
+    // Narrow projections (fewer than two bands of the kernel below per SIMD)
     // split the hidden dimension over the waves of a workgroup instead, when
-    // its LDS (windows and tile sums) stays within 64 KiB. The VALU kernels'
-    // time grows with the row count while the MFMA kernel's 16-row tile costs
-    // the same for 1..16 rows: from 9 rows (11 with the split kernel) the MFMA
-    // kernel is the faster one (15 rows on 129280 x 7168: 261 -> 178 us, on
-    // 7168 x 18432: 67 -> 48 us), with the same bits.
-    constexpr int kValuMax = 8, kSplitMax = 10;
+    // its LDS (windows and tile sums) stays within 64 KiB.
     const int T_main = R <= 4 ? 2 : 4;
     const int64_t bands_main = (V + 8 * T_main - 1) / (8 * T_main);
     const int NT = (H + kW8TileK - 1) / kW8TileK;
-    const bool split = bands_main < (int64_t)dev.num_cus * 8 &&
-                       split_lds_bytes<kSplitMax, 4>(NT < 8 ? NT : 8, NT) <= 65536;
-    if (R >= 1 && R <= kSplitMax && split) {
+    if (R >= 1 && R < 16 && bands_main < (int64_t)dev.num_cus * 8 &&
+        split_lds_bytes<15, 4>(NT < 8 ? NT : 8, NT) <= 65536) {
         switch (R) {
 #define QH_W8_SPLIT(RR)   \
     case RR:              \
@@ -1106,12 +1098,17 @@ hipError_t run_w8a8_gemv(const uint8_t* W, const float* sw, const uint8_t* xq, c
             QH_W8_SPLIT(8)
             QH_W8_SPLIT(9)
             QH_W8_SPLIT(10)
+            QH_W8_SPLIT(11)
+            QH_W8_SPLIT(12)
+            QH_W8_SPLIT(13)
+            QH_W8_SPLIT(14)
+            QH_W8_SPLIT(15)
 #undef QH_W8_SPLIT
             default:
                 break;
         }
     }
-    if (!split) switch (R) {
+    switch (R) {
 #define QH_W8_VALU(RR, TT, WV, MB, BPC)                                                   \
     case RR:                                                                              \
         return launch_valu<RR, TT, WV, MB, BPC>(W, sw, xq, sa, H, V, out, dev, stream);
@@ -1123,12 +1120,18 @@ hipError_t run_w8a8_gemv(const uint8_t* W, const float* sw, const uint8_t* xq, c
         QH_W8_VALU(6, 4, 8, 4, 1)
         QH_W8_VALU(7, 4, 8, 4, 1)
         QH_W8_VALU(8, 4, 8, 4, 1)
+        QH_W8_VALU(9, 4, 8, 2, 1)
+        QH_W8_VALU(10, 4, 8, 2, 1)
+        QH_W8_VALU(11, 4, 8, 2, 1)
+        QH_W8_VALU(12, 4, 8, 2, 1)
+        QH_W8_VALU(13, 4, 8, 2, 1)
+        QH_W8_VALU(14, 4, 8, 2, 1)
+        QH_W8_VALU(15, 4, 8, 2, 1)
 #undef QH_W8_VALU
         default:
             break;
     }
-    if (R < 1 || R > 128) return hipErrorInvalidValue;
-    static_assert(kValuMax < 16 && kSplitMax < 16, "rows the VALU kernels leave fit a row tile");
+    if (R < 16 || R > 128) return hipErrorInvalidValue;
     // Launch shapes <RT, vocab tiles per workgroup, waves per tile, weight
     // slabs in flight>, eight waves per workgroup (two per SIMD): up to 32
     // rows one wave per tile, up to 64 two, above four (2 chains each).
