@@ -174,17 +174,29 @@ nvfp4_gemv_kernel(const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ bs
                         }
                         const float b0 = __builtin_amdgcn_cvt_f32_fp8(cur.sc[t], 0);
                         const float b1 = __builtin_amdgcn_cvt_f32_fp8(cur.sc[t], 1);
+                        // The 2R block chains advance side by side, one
+                        // dot2 each per step (a chain's next dot2 is 2R
+                        // instructions away); each still sums its 8 pairs in
+                        // order.
+                        float p0[R], p1[R];
 #pragma unroll
                         for (int r = 0; r < R; ++r) {
-                            float p0 = dot2_bf16_zero(xv[r][0], wb[0]);
-                            float p1 = dot2_bf16_zero(xv[r][8], wb[8]);
+                            p0[r] = dot2_bf16_zero(xv[r][0], wb[0]);
+                            p1[r] = dot2_bf16_zero(xv[r][8], wb[8]);
+                        }
 #pragma unroll
-                            for (int p = 1; p < 8; ++p) p0 = dot2_bf16(xv[r][p], wb[p], p0);
+                        for (int p = 1; p < 8; ++p) {
 #pragma unroll
-                            for (int p = 9; p < 16; ++p) p1 = dot2_bf16(xv[r][p], wb[p], p1);
+                            for (int r = 0; r < R; ++r) {
+                                p0[r] = dot2_bf16(xv[r][p], wb[p], p0[r]);
+                                p1[r] = dot2_bf16(xv[r][p + 8], wb[p + 8], p1[r]);
+                            }
+                        }
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
                             float a = acc[r * T + t];
-                            a = __builtin_fmaf(b0, p0, a);
-                            a = __builtin_fmaf(b1, p1, a);
+                            a = __builtin_fmaf(b0, p0[r], a);
+                            a = __builtin_fmaf(b1, p1[r], a);
                             acc[r * T + t] = a;
                         }
                     }
@@ -224,17 +236,30 @@ nvfp4_gemv_kernel(const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ bs
                         xv[4 * c + 2] = xr[r & 1][c].z;
                         xv[4 * c + 3] = xr[r & 1][c].w;
                     }
+                    // The 2T block chains of this row advance side by
+                    // side, one dot2 each per step, so a chain's next dot2
+                    // is 2T instructions away (a lone chain of dependent
+                    // dot2 issues well below the VALU's rate); each still
+                    // sums its 8 pairs in order.
+                    float p0[T], p1[T];
 #pragma unroll
                     for (int t = 0; t < T; ++t) {
-                        float p0 = dot2_bf16_zero(xv[0], wb[t][0]);
-                        float p1 = dot2_bf16_zero(xv[8], wb[t][8]);
+                        p0[t] = dot2_bf16_zero(xv[0], wb[t][0]);
+                        p1[t] = dot2_bf16_zero(xv[8], wb[t][8]);
+                    }
 #pragma unroll
-                        for (int p = 1; p < 8; ++p) p0 = dot2_bf16(xv[p], wb[t][p], p0);
+                    for (int p = 1; p < 8; ++p) {
 #pragma unroll
-                        for (int p = 9; p < 16; ++p) p1 = dot2_bf16(xv[p], wb[t][p], p1);
+                        for (int t = 0; t < T; ++t) {
+                            p0[t] = dot2_bf16(xv[p], wb[t][p], p0[t]);
+                            p1[t] = dot2_bf16(xv[p + 8], wb[t][p + 8], p1[t]);
+                        }
+                    }
+#pragma unroll
+                    for (int t = 0; t < T; ++t) {
                         float a = acc[r * T + t];
-                        a = __builtin_fmaf(bsf[t][0], p0, a);
-                        a = __builtin_fmaf(bsf[t][1], p1, a);
+                        a = __builtin_fmaf(bsf[t][0], p0[t], a);
+                        a = __builtin_fmaf(bsf[t][1], p1[t], a);
                         acc[r * T + t] = a;
                     }
                 }
