@@ -100,7 +100,7 @@ __device__ __forceinline__ void q6_stage_tile(Q6Lds<R>& L, const uint8_t* q8, in
     }
 }
 
-template <int R, int T, int WAVES, int MAXB, int BPC>
+template <int R, int T, int WAVES, int MAXB, int BPC, int DEPTH>
 __global__ void __launch_bounds__(WAVES * kWave, (WAVES * BPC + 3) / 4)
 q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ q8, int H, int V,
                 uint16_t* __restrict__ out, int nsuper) {
@@ -111,12 +111,12 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     static_assert(NP <= 64 && R <= 8, "T*R must be <= 64, R <= 8");
     static_assert(kItemBytes + 15 <= 64 * 16, "an item must fit one 16-byte load per lane");
     static_assert((kItemBytes + 13) / 16 + 2 <= 61, "the shifted chunks stay in the row's buffer");
-    static_assert(T <= 63, "vmcnt counts the loads of one item");
+    static_assert(DEPTH >= 2 && (DEPTH - 1) * T <= 63, "vmcnt counts the loads of the items in flight");
     __shared__ Q6Lds<R> L;
-    // wave-private weight staging, two buffers: [wave][item parity][row t]
-    // [1024 bytes]. Item it + 1 is loaded into one buffer at the start of
-    // step it, while item it is read from the other.
-    __shared__ u32x4_t WB[WAVES][2][T][kWave];
+    // wave-private weight staging, a ring of DEPTH buffers: [wave][item %
+    // DEPTH][row t][1024 bytes]. Item it + DEPTH - 1 is loaded into one
+    // buffer at the start of step it, while item it is read from another.
+    __shared__ u32x4_t WB[WAVES][DEPTH][T][kWave];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -149,7 +149,7 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     // The offsets count from the block's first staging buffer and include
     // this wave's buffers (a multiple of 4 bytes).
     const int qh_back = hi_shift < 4 ? 1 : 0;
-    const int p_sb = wave * (2 * T * kWave * 16) + sbi * kQ6KBlockBytes + (sbi >= 2 ? 32 : 0);
+    const int p_sb = wave * (DEPTH * T * kWave * 16) + sbi * kQ6KBlockBytes + (sbi >= 2 ? 32 : 0);
     const int p_ql = p_sb + ql_off;
     const int p_qh = p_sb + qh_off - qh_back;
     const int b_qh = 8 * qh_back + hi_shift - 4;
@@ -227,11 +227,12 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
 
             float acc[NP];
             int bi = 0, s = 0;
-            // (pbi, ps): the next item to load. Step it loads item it + 1 into
-            // the buffer that step it - 1 read (all its reads were consumed
-            // there), then waits for item it: T loads (item it + 1's) may
-            // stay in flight, none once the last item is loaded. Nothing else
-            // in this loop loads from vector memory, so the count is exact.
+            // (pbi, ps): the next item to load. Step it loads item it + DEPTH
+            // - 1 into the buffer that step it - 1 read (all its reads were
+            // consumed there), then waits for item it: the T loads of each
+            // item after it that is already issued may stay in flight
+            // (DEPTH - 1 items, fewer at the end). Nothing else in this loop
+            // loads from vector memory, so the count is exact.
             int pbi = 0, ps = 0;
             auto load_next = [&](int buf) __attribute__((always_inline)) {
                 issue(pbi, ps, buf);
@@ -240,13 +241,16 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                     ++pbi;
                 }
             };
-            auto step = [&](int it) __attribute__((always_inline)) {
-                const int buf = it & 1;
-                if (it + 1 < nitems) {
-                    load_next(buf ^ 1);
-                    wait_vmcnt<T>();
+            auto step = [&](int it, int buf) __attribute__((always_inline)) {
+                if (it + DEPTH - 1 < nitems) {
+                    load_next(buf == 0 ? DEPTH - 1 : buf - 1);
+                    wait_vmcnt<(DEPTH - 1) * T>();
                 } else {
-                    wait_vmcnt<0>();
+                    // items it + 1 .. nitems - 1 are in flight (wave-uniform)
+                    const int left = nitems - 1 - it;
+                    static_for<DEPTH - 1>([&](auto i) __attribute__((always_inline)) {
+                        if (left == decltype(i)::value) wait_vmcnt<decltype(i)::value * T>();
+                    });
                 }
                 if (s == 0) {
 #pragma unroll
@@ -321,9 +325,13 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
                     ++s;
                 }
             };
-            if (nitems > 0) load_next(0);
+            for (int j = 0; j < DEPTH - 1 && j < nitems; ++j) load_next(j);
+            int buf = 0;
 #pragma unroll 1
-            for (int it = 0; it < nitems; ++it) step(it);
+            for (int it = 0; it < nitems; ++it) {
+                step(it, buf);
+                buf = buf + 1 == DEPTH ? 0 : buf + 1;
+            }
         }
 
 #pragma unroll
@@ -335,7 +343,7 @@ q6k_gemv_kernel(const uint8_t* __restrict__ blocks, const uint8_t* __restrict__ 
     }
 }
 
-template <int R, int T, int WAVES, int MAXB, int BPC>
+template <int R, int T, int WAVES, int MAXB, int BPC, int DEPTH>
 static hipError_t launch_q6k(const uint8_t* blocks, const uint8_t* q8, int H, int V,
                              uint16_t* out, const DeviceInfo& dev, hipStream_t stream) {
     const int64_t NB = (V + T - 1) / T;
@@ -344,7 +352,7 @@ static hipError_t launch_q6k(const uint8_t* blocks, const uint8_t* q8, int H, in
     const int64_t TW = nblk * WAVES;
     const int64_t per_wave = (NB + TW - 1) / TW;
     const int nsuper = (int)((per_wave + MAXB - 1) / MAXB);
-    hipLaunchKernelGGL((q6k_gemv_kernel<R, T, WAVES, MAXB, BPC>), dim3((unsigned)nblk),
+    hipLaunchKernelGGL((q6k_gemv_kernel<R, T, WAVES, MAXB, BPC, DEPTH>), dim3((unsigned)nblk),
                        dim3(WAVES * kWave), 0, stream, blocks, q8, H, V, out, nsuper);
     return hipGetLastError();
 }
@@ -352,17 +360,17 @@ static hipError_t launch_q6k(const uint8_t* blocks, const uint8_t* q8, int H, in
 hipError_t run_q6k(const uint8_t* blocks, const uint8_t* q8, int R, int H, int V, uint16_t* out,
                    const DeviceInfo& dev, hipStream_t stream) {
     switch (R) {
-#define QH_Q6_CASE(RR, TT, WV, MB, BPC) \
-    case RR:                            \
-        return launch_q6k<RR, TT, WV, MB, BPC>(blocks, q8, H, V, out, dev, stream);
-        QH_Q6_CASE(1, 4, 8, 12, 2)
-        QH_Q6_CASE(2, 2, 12, 8, 2)
-        QH_Q6_CASE(3, 4, 12, 12, 1)
-        QH_Q6_CASE(4, 4, 12, 12, 1)
-        QH_Q6_CASE(5, 4, 12, 12, 1)
-        QH_Q6_CASE(6, 4, 8, 12, 1)
-        QH_Q6_CASE(7, 4, 8, 12, 1)
-        QH_Q6_CASE(8, 4, 8, 12, 1)
+#define QH_Q6_CASE(RR, TT, WV, MB, BPC, DP) \
+    case RR:                                \
+        return launch_q6k<RR, TT, WV, MB, BPC, DP>(blocks, q8, H, V, out, dev, stream);
+        QH_Q6_CASE(1, 4, 8, 12, 2, 2)
+        QH_Q6_CASE(2, 2, 12, 8, 2, 2)
+        QH_Q6_CASE(3, 4, 12, 12, 1, 2)
+        QH_Q6_CASE(4, 4, 12, 12, 1, 2)
+        QH_Q6_CASE(5, 4, 12, 12, 1, 2)
+        QH_Q6_CASE(6, 4, 8, 12, 1, 2)
+        QH_Q6_CASE(7, 4, 8, 12, 1, 2)
+        QH_Q6_CASE(8, 4, 8, 12, 1, 2)
 #undef QH_Q6_CASE
         default:
             return hipErrorInvalidValue;
