@@ -324,19 +324,19 @@ hipError_t run_nvfp4(const uint8_t* Wp, const uint8_t* bs, const uint16_t* x, fl
         QH_F4_CASE(1, 2, 16, 20, 1)
         QH_F4_CASE(2, 4, 8, 8, 2)
         QH_F4_CASE(3, 2, 8, 12, 2)
-        QH_F4_CASE(4, 2, 8, 12, 2)
+        QH_F4_CASE(4, 4, 12, 12, 1)
         QH_F4_CASE(5, 4, 8, 12, 1)
         QH_F4_CASE(6, 4, 8, 12, 1)
         QH_F4_CASE(7, 4, 8, 12, 1)
         QH_F4_CASE(8, 4, 8, 12, 1)
-        QH_F4_CASE(9, 4, 8, 12, 1)
-        QH_F4_CASE(10, 4, 8, 12, 1)
-        QH_F4_CASE(11, 4, 8, 12, 1)
-        QH_F4_CASE(12, 4, 8, 12, 1)
-        QH_F4_CASE(13, 4, 8, 12, 1)
-        QH_F4_CASE(14, 4, 8, 12, 1)
-        QH_F4_CASE(15, 4, 8, 12, 1)
-        QH_F4_CASE(16, 4, 8, 12, 1)
+        QH_F4_CASE(9, 4, 8, 20, 1)
+        QH_F4_CASE(10, 4, 8, 20, 1)
+        QH_F4_CASE(11, 4, 8, 20, 1)
+        QH_F4_CASE(12, 4, 8, 20, 1)
+        QH_F4_CASE(13, 4, 8, 20, 1)
+        QH_F4_CASE(14, 4, 8, 20, 1)
+        QH_F4_CASE(15, 4, 8, 20, 1)
+        QH_F4_CASE(16, 4, 8, 20, 1)
 #undef QH_F4_CASE
         default:
             return hipErrorInvalidValue;
