@@ -20,14 +20,15 @@
 // wave covers four super-blocks (1024 weights, 840 bytes) of each of its T
 // vocab rows per item. Those 840 bytes are the aligned 16-byte chunks that
 // hold them (a chunk holding at least one byte of the item never crosses a
-// page), loaded straight into one of two wave-private LDS buffers by one
-// fully coalesced global_load_lds_dwordx4 per row (lane l's chunk to slot
-// l); each lane then reads its fields from LDS as aligned dwords and cuts
-// four 6-bit codes at a time out of them with v_alignbit funnel shifts
-// (super-blocks are only 2-byte aligned; the shift folds the misalignment
-// and the field's bit position). While item it is computed from one buffer,
-// item it + 1 is in flight into the other; the wait before each item is
-// placed by hand (lds_dma16), so that the next item's loads stay in flight
+// page), loaded straight into one of a ring of DEPTH wave-private LDS
+// buffers (two in every launch shape) by one fully coalesced
+// global_load_lds_dwordx4 per row (lane l's chunk to slot l); each lane then
+// reads its fields from LDS as aligned dwords and cuts four 6-bit codes at a
+// time out of them with v_alignbit funnel shifts (super-blocks are only
+// 2-byte aligned; the shift folds the misalignment and the field's bit
+// position). While item it is computed from one buffer, items it + 1 ..
+// it + DEPTH - 1 are in flight into the others; the wait before each item is
+// placed by hand (lds_dma16), so that the later items' loads stay in flight
 // across the computation. With no register ring, the weights cost no
 // registers between issue and use. The -32 offset is folded into the
 // integer dot: the staging step stores -32 * sum(q8) per sub-block next to
