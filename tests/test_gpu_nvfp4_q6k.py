@@ -73,7 +73,7 @@ def _nvfp4_small(V, H, cfg=synth.NVFP4_Q6K_129280X7168):
 
 def test_nvfp4_edge_shapes(qh):
     for V, H, rows in [(1, 32, 1), (1001, 2080, 8), (77, 8224, 3), (513, 7168, 13),
-                       (4096, 64, 9)]:
+                       (4096, 64, 9), (1001, 2080, 4), (1003, 8224, 16), (6, 12320, 4)]:
         log(f"[case] nvfp4 edge V={V} H={H} rows={rows}")
         wp, bs, g = _nvfp4_small(V, H)
         x = synth.activations_bf16(synth.NVFP4_Q6K_129280X7168, rows, hidden=H, max_rows=rows)
